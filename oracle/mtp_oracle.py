@@ -346,9 +346,12 @@ def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int
     lse_v = logsumexp_rows(zv / Te)
     y = argmax_lowest_f32(zv)
     y_margin = top2_gap(zv)
-    if T > 0:
+    if zd_raw is not None:
+        # draft-row flags are reported at any temperature; q itself is used only when T > 0
         zd, dflags = sanitize(zd_raw)
         lse_d = logsumexp_rows(zd / Te)
+    elif T > 0:
+        raise ValueError("sampled acceptance needs the draft logits")
     else:
         dflags = np.zeros((B, k), dtype=np.uint32)
 
