@@ -1,0 +1,260 @@
+"""Throughput of one native-MTP speculative cycle on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload model_greedy]
+
+One step = one whole cycle of the hot path over one batch of synthetic input:
+k draft-head calls (first 64,000 rows of a 152,064 x 2560 bf16 head, one hidden row per
+request), one verify pass over the k+1 = 8 rows, acceptance, and the commit of the
+accepted row's recurrent-state snapshot (36 layers x 16 heads x 128 x 128 fp32 = 36 MiB
+per snapshot, 8 snapshots) with the trim of rejected KV rows (12 layers, fp16 4 x 256).
+Inputs are resident in HBM before the timed region.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "verify cycles/s (k=7, V=152,064, d=2560 bf16) + achieved HBM GB/s vs peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_head_amd", "csrc", "lmhead.hip")
+
+# recurrent state and KV per request (the model's 36 recurrent layers x 16 heads x 128x128
+# fp32, 12 attention layers with fp16 4 x 256 KV rows)
+STATE_LAYERS, STATE_HEADS, STATE_DIM = 36, 16, 128
+KV_LAYERS, KV_HEADS, KV_DIM, KV_ROWS = 12, 4, 256, 64
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="model_greedy", choices=["model_greedy", "q4_greedy", "q4_sampled"])
+    ap.add_argument("--cpu-cycles", type=int, default=0, help="oracle cycles for the CPU baseline (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-commit", action="store_true", help="leave the commit out of the step")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel: str, units_per_launch: float):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_digest") != source_digest():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import speculative_decoding_head_amd as mtp
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+
+    # ---- inputs (seeded, synthetic), resident in HBM -----------------------------
+    t0 = time.time()
+    rng = np.random.default_rng(wl.seed)
+    head = synth.make_head(rng, wl.V, wl.d, wl.wtype)
+    h_v, h_d = synth.make_hidden(rng, wl.B, wl.k, wl.d)
+    hv = synth.encode_hidden(h_v, wl.htype)
+    hd = synth.encode_hidden(h_d, wl.htype)
+    if wl.wtype == "bf16":
+        dh = mtp.Head(mtp.W_BF16, wl.d, wl.V, torch.from_numpy(head.w.view(np.int16)).to(dev))
+    else:
+        dh = mtp.Head(mtp.W_Q4A32, wl.d, wl.V, torch.from_numpy(head.w).to(dev),
+                      torch.from_numpy(head.scale.view(np.int16)).to(dev),
+                      torch.from_numpy(head.minv.view(np.int16)).to(dev))
+    B, k, nd, V, d, T = wl.B, wl.k, wl.n_draft, wl.V, wl.d, wl.temperature
+    hv_t = torch.from_numpy(hv.view(np.int16)).to(dev)                          # [B][k+1][d]
+    hd_slots = [torch.from_numpy(np.ascontiguousarray(hd[:, i]).view(np.int16)).to(dev) for i in range(k)]
+    dtok = torch.zeros(B, k, dtype=torch.int32, device=dev)
+    dst = mtp.row_stats_empty(B, k)
+    dlg = torch.zeros(B, k, nd, dtype=torch.float32, device=dev) if T > 0 else None
+    vst = mtp.row_stats_empty(B, k + 1)
+    vlg = torch.zeros(B, k + 1, V, dtype=torch.float32, device=dev) if T > 0 else None
+    out = torch.zeros(B, k + 1, dtype=torch.int32, device=dev)
+    nacc = torch.zeros(B, dtype=torch.int32, device=dev)
+    nemit = torch.zeros(B, dtype=torch.int32, device=dev)
+    flg = torch.zeros(B, dtype=torch.int32, device=dev)
+    ws = mtp.workspace(max(mtp.workspace_bytes(mtp.OP_DRAFT, B, nd, B),
+                           mtp.workspace_bytes(mtp.OP_VERIFY, B * (k + 1), V, B),
+                           mtp.workspace_bytes(mtp.OP_ACCEPT, 0, V, B)))
+    with_commit = not args.no_commit
+    state_bytes = STATE_LAYERS * STATE_HEADS * STATE_DIM * STATE_DIM * 4
+    kv_row_bytes = KV_HEADS * KV_DIM * 2
+    if with_commit:
+        g = torch.Generator(device=dev).manual_seed(1)
+        snaps = torch.randint(0, 256, (B, k + 1, state_bytes), dtype=torch.uint8, device=dev, generator=g)
+        live = torch.zeros(B, state_bytes, dtype=torch.uint8, device=dev)
+        # room for every cycle's accepted rows, so the trim never saturates at the cache end
+        kv_rows = KV_ROWS + (k + 1) * (args.warmup + args.steps)
+        kv = torch.zeros(B, KV_LAYERS, 2, kv_rows, kv_row_bytes, dtype=torch.uint8, device=dev)
+        kv_len = torch.zeros(B, dtype=torch.int32, device=dev)
+    setup_s = time.time() - t0
+
+    stream = torch.cuda.current_stream()
+
+    def cycle(c, events=None):
+        smp = mtp.sampling(T, wl.eos, wl.philox_seed, c, 0)
+        if events is not None:
+            events[0].record(stream)
+        for i in range(k):
+            mtp.mtp_draft_head(dh, nd, hd_slots[i], i, k, smp, dtok, dst, dlg, ws, stream)
+            if events is not None:
+                events[1 + i].record(stream)
+        mtp.mtp_verify_logits(dh, hv_t, k, dtok, k, smp, vst, vlg, ws, stream)
+        if events is not None:
+            events[k + 1].record(stream)
+        mtp.mtp_accept_sample(B, k, k, V, nd, smp, dtok, dst, dlg, vst, vlg, out, nacc, nemit, flg, ws, stream)
+        if events is not None:
+            events[k + 2].record(stream)
+        if with_commit:
+            mtp.mtp_commit_state(B, k, nacc, snaps, live, state_bytes, kv, KV_LAYERS, kv_rows, kv_row_bytes,
+                                 kv_len, stream)
+            if events is not None:
+                events[k + 3].record(stream)
+
+    for c in range(args.warmup):
+        cycle(c)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K cycles, per-kernel HIP events on the launch stream --------
+    n_ev = k + 4
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        cycle(args.warmup + s, evs[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+
+    draft_ms = [evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps) for i in range(k)]
+    verify_ms = [evs[s][k].elapsed_time(evs[s][k + 1]) for s in range(args.steps)]
+    accept_ms = [evs[s][k + 1].elapsed_time(evs[s][k + 2]) for s in range(args.steps)]
+    commit_ms = ([evs[s][k + 2].elapsed_time(evs[s][k + 3]) for s in range(args.steps)] if with_commit else [0.0])
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = args.steps / elapsed
+
+    # algorithmic bytes per launch (weights read once, hidden rows, outputs)
+    wrow = {"bf16": d * 2, "q4a32": d // 2 + 2 * 2 * (d // 32)}[wl.wtype]
+    hbytes = d * 2
+    draft_bytes = nd * wrow + B * hbytes + B * (32 + 4) + (B * nd * 4 if T > 0 else 0)
+    verify_bytes = V * wrow + B * (k + 1) * hbytes + B * (k + 1) * 32 + (B * (k + 1) * V * 4 if T > 0 else 0)
+    commit_bytes = (2 * B * state_bytes) if with_commit else 0
+    cycle_bytes = k * draft_bytes + verify_bytes + commit_bytes
+    d_avg = float(np.mean(draft_ms)) * 1e-3
+    v_avg = float(np.mean(verify_ms)) * 1e-3
+
+    def roof(bytes_per_launch, avg_s, kernel):
+        ach = bytes_per_launch / avg_s / 1e9
+        tr = load_traffic(kernel, 1)
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": tr,
+                "kernel": kernel, "avg_launch_us": round(avg_s * 1e6, 2),
+                "algorithmic_bytes_per_launch": int(bytes_per_launch)}
+
+    draft_kernel = "mtp_draft_head_kernel"
+    verify_kernel = "mtp_verify_logits_kernel"
+    dominant = "draft" if k * d_avg >= v_avg else "verify"
+    roofline = roof(draft_bytes, d_avg, draft_kernel) if dominant == "draft" else roof(verify_bytes, v_avg, verify_kernel)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "cycles/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.wtype == "bf16" else "q4a32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "d": d, "V": V, "n_draft": nd, "k": k, "batch": B,
+                   "temperature": T, "weights": wl.wtype, "accumulate": "fp32",
+                   "step": f"{k} draft-head calls + verify ({B * (k + 1)} rows) + accept"
+                           + (" + commit (36 MiB snapshot select, 12-layer KV trim)" if with_commit else "")},
+        "roofline": roofline,
+        "roofline_verify": roof(verify_bytes, v_avg, verify_kernel),
+        "stages_us": {"draft_head_avg": round(d_avg * 1e6, 2), "verify_avg": round(v_avg * 1e6, 2),
+                      "accept_avg": round(float(np.mean(accept_ms)) * 1e3, 2),
+                      "commit_avg": round(float(np.mean(commit_ms)) * 1e3, 2)},
+        "cycle_algorithmic_GBps": round(cycle_bytes * value / 1e9, 1),
+        "tokens_per_s": round(float(nemit.sum().item()) * value, 1),
+        "setup_s": round(setup_s, 1),
+    }
+
+    # ---- CPU baseline: the oracle, as it stands, on a bounded sample --------------
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, head, hv, hd, args.cpu_cycles, with_commit, state_bytes)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, head, hv, hd, n_cycles, with_commit, state_bytes):
+    from oracle import mtp_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas = ",".join(sorted({p.get("internal_api", "?") for p in threadpool_info()}))
+    except Exception:  # pragma: no cover
+        threads, blas = os.cpu_count(), "unknown"
+    W = O.head_weights_f64(head)                      # setup, not timed
+    hv64 = O.hidden_f64(hv, wl.htype)
+    hd64 = O.hidden_f64(hd, wl.htype)
+    delta = 2e-2
+    if with_commit:
+        snaps = np.zeros((wl.B, wl.k + 1, state_bytes), np.uint8)
+        live = np.zeros((wl.B, state_bytes), np.uint8)
+        kv = np.zeros((wl.B, KV_LAYERS, 2, KV_ROWS, KV_HEADS * KV_DIM * 2), np.uint8)
+        kv_len = np.zeros(wl.B, np.int32)
+    budget_s = 20.0
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        o = O.cycle(W, wl.n_draft, hd64, hv64, wl.temperature, wl.philox_seed, done, wl.eos, delta)
+        if with_commit:
+            O.commit(snaps, live, kv, kv_len, o["accept"]["n_accept"], wl.k)
+        done += 1
+        el = time.perf_counter() - t0
+        if (n_cycles and done >= n_cycles) or (not n_cycles and el >= budget_s):
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(done / el, 4), "unit": "cycles/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} whole cycles of the {wl.name} workload (numpy fp64, weights pre-converted "
+                      f"to fp64 outside the timing), {el:.1f} s",
+            "blas": blas, "cpu": platform.processor() or platform.machine(),
+            "host_cores_visible": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

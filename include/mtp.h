@@ -1,0 +1,236 @@
+/*
+ * mtp.h - C ABI of one native-MTP speculative decoding cycle on an MI355X (gfx950).
+ *
+ * One cycle, as the pages describe it:
+ *   draft   k times: the truncated-vocabulary draft head (the first n_draft rows of
+ *           the shared LM head) scores one hidden row per request and picks the next
+ *           draft token on the GPU; the token stays in device memory and feeds the
+ *           next draft (lucebox-hub PR "feat(qwen4exp): MTP speculative decoding",
+ *           section "What");
+ *   verify  the trunk's k+1 verify rows get full-vocabulary logits in one batched
+ *           pass, with softmax statistics at temperature T (same section);
+ *   accept  exact match at T = 0 (same PR, section "Exactness"), or probability-ratio
+ *           acceptance u*q <= p with a max(0, p - q) residual resample at the first
+ *           rejection, zero/non-finite probabilities handled and EOS inside the block
+ *           truncating (DS4Server issue "Add Qwen3.8 Flash Next native MTP
+ *           speculation", section "Implementation" and closing comment "Review");
+ *   commit  the accepted row's recurrent-state snapshot becomes live and the
+ *           rejected KV rows are trimmed (same issue, "Implementation"; llama.cpp PR
+ *           "qwen4exp : port NextN/MTP speculative decoding to master", commit "keep
+ *           speculative checkpoints on device").
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or synchronises; each call only enqueues kernels on `stream`
+ *     (a hipStream_t; NULL = the default stream) and returns.  Inputs and outputs must
+ *     stay alive until the stream has run the work.
+ *   - Host structs (mtp_head, mtp_sampling) are read during the call only.
+ *   - Return value: MTP_OK, or a negative mtp_status from argument validation or from
+ *     the kernel launch.  Validation failures enqueue nothing.  Outcomes that depend on
+ *     device data (non-finite logits, EOS, residual fallback, out-of-range n_accept) are
+ *     reported through device-side flags, never by the return value.
+ *   - No global mutable state: calls are thread-safe.  Calls that share a workspace
+ *     must be ordered on one stream.
+ *   - Row-major layouts throughout; all tensors contiguous; every pointer 16-byte
+ *     aligned.
+ */
+#ifndef MTP_H_
+#define MTP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MTP_ABI_VERSION 1
+
+/* ---------------------------------------------------------------------------------- */
+/* status codes                                                                        */
+/* ---------------------------------------------------------------------------------- */
+typedef enum mtp_status {
+  MTP_OK = 0,
+  MTP_ERR_NULL = -1,      /* a required pointer is NULL                                 */
+  MTP_ERR_SHAPE = -2,     /* a size is out of range (k, B, d, vocab, n_draft, rows...)  */
+  MTP_ERR_DTYPE = -3,     /* unknown weight or hidden type, or an unsupported pairing   */
+  MTP_ERR_RANGE = -4,     /* temperature negative or not finite; slot >= k_max; ...     */
+  MTP_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned                           */
+  MTP_ERR_WORKSPACE = -6, /* workspace missing or smaller than mtp_workspace_bytes()    */
+  MTP_ERR_HIP = -7        /* the HIP runtime reported an error at launch                */
+} mtp_status;
+
+/* ---------------------------------------------------------------------------------- */
+/* shared LM head                                                                      */
+/* ---------------------------------------------------------------------------------- */
+typedef enum mtp_wtype {
+  MTP_W_F32 = 0,   /* w: float [vocab][d]                                              */
+  MTP_W_BF16 = 1,  /* w: bf16 bit patterns, uint16 [vocab][d]                          */
+  MTP_W_Q4A32 = 2  /* 4-bit affine, 32-value groups along d (DS4Server issue above,
+                      closing comment "Implementation"):  w[x][32g+j] = scale*q + min,
+                      q = unsigned nibble j of group g;
+                        w:     uint8 [vocab][d/2], element 2m in the low nibble of byte m,
+                               element 2m+1 in the high nibble;
+                        scale: bf16 [vocab][d/32];  minv: bf16 [vocab][d/32]            */
+} mtp_wtype;
+
+typedef enum mtp_htype {
+  MTP_H_F32 = 0,   /* hidden rows: float [rows][d]                                     */
+  MTP_H_BF16 = 1   /* hidden rows: bf16 bit patterns, uint16 [rows][d]                 */
+} mtp_htype;
+
+/* Supported pairings: F32 weights with F32 hiddens; BF16 or Q4A32 weights with BF16
+ * hiddens.  d must be a positive multiple of 32; vocab >= 1. */
+typedef struct mtp_head {
+  int32_t wtype;       /* mtp_wtype                                                    */
+  int32_t d;           /* hidden size                                                  */
+  int32_t vocab;       /* V, rows of the shared head                                   */
+  int32_t reserved;    /* must be 0                                                    */
+  const void* w;       /* device, layout per wtype                                     */
+  const void* scale;   /* device, Q4A32 only (else NULL)                               */
+  const void* minv;    /* device, Q4A32 only (else NULL)                               */
+} mtp_head;
+
+/* ---------------------------------------------------------------------------------- */
+/* sampling parameters                                                                 */
+/* ---------------------------------------------------------------------------------- */
+/* Random draws use Philox4x32-10 (Salmon et al., SC'11): key = (seed lo32, seed hi32),
+ * counter = (x >> 2, stream << 8 | row, request_base + b, cycle), word x & 3, where x is
+ * the vocabulary id (0 for the acceptance uniform).  Streams: 0 draft sample, 1
+ * acceptance uniform, 2 correction/bonus sample.  Uniforms: acceptance
+ * u = ((w >> 8) + 1) * 2^-24 in (0, 1]; Gumbel u = (2 (w >> 9) + 1) * 2^-24 in (0, 1),
+ * noise -ln(-ln u).  Every categorical draw is argmax(z/T + noise), lowest id on ties. */
+typedef struct mtp_sampling {
+  float temperature;     /* T >= 0; 0 = greedy (argmax drafts, exact-match acceptance) */
+  int32_t eos_id;        /* end-of-sequence id, or -1 for none                          */
+  uint64_t seed;         /* Philox key                                                  */
+  uint32_t cycle;        /* cycle counter; a new value gives fresh draws                */
+  uint32_t request_base; /* counter index of request 0 of this call                     */
+} mtp_sampling;
+
+/* ---------------------------------------------------------------------------------- */
+/* per-row results of the draft head and the verify pass (32 bytes)                    */
+/* ---------------------------------------------------------------------------------- */
+/* Logits are sanitised before any statistic: NaN -> -inf; a row holding +inf becomes
+ * 0 at its +inf ids and -inf elsewhere (uniform over them).  T_eff = T, or 1 when T = 0. */
+typedef struct mtp_row_stats {
+  float max;         /* max of the sanitised logits (-inf if every one is -inf)         */
+  float lse;         /* log sum exp(z / T_eff) of the sanitised logits                  */
+  float z_tok;       /* sanitised logit of this row's token of interest:
+                        draft rows - the picked draft token;
+                        verify row i < k - the drafted token d_{i+1}; row k - -inf      */
+  int32_t argmax;    /* lowest-id argmax; -1 if the row is invalid                      */
+  int32_t sample;    /* argmax(z/T + Gumbel) at T > 0, = argmax at T = 0; -1 if invalid  */
+  uint32_t flags;    /* MTP_ROW_* bits                                                 */
+  int32_t n_posinf;  /* number of +inf logits in the row                                */
+  int32_t reserved;
+} mtp_row_stats;
+
+#define MTP_ROW_NONFINITE 0x1u   /* the row held NaN or +-inf                           */
+#define MTP_ROW_POSINF 0x2u      /* the row held +inf and was made uniform over those ids */
+#define MTP_ROW_INVALID 0x4u     /* every sanitised logit is -inf                       */
+
+/* per-request acceptance flags */
+#define MTP_ACC_ALL_ACCEPTED 0x01u     /* all k drafts accepted; a bonus token emitted  */
+#define MTP_ACC_EOS 0x02u              /* the block ends with eos_id                     */
+#define MTP_ACC_RESID_FALLBACK 0x04u   /* empty residual; the correction was drawn from p */
+#define MTP_ACC_ROW_INVALID 0x08u      /* a target row was all -inf: no token after it   */
+#define MTP_ACC_NONFINITE_TARGET 0x10u /* a target row examined held NaN/+-inf           */
+#define MTP_ACC_NONFINITE_DRAFT 0x20u  /* a draft row examined held NaN/+-inf            */
+#define MTP_ACC_DRAFT_INVALID 0x40u    /* a draft token was -1 (all -inf draft row)      */
+
+/* ---------------------------------------------------------------------------------- */
+/* workspace                                                                           */
+/* ---------------------------------------------------------------------------------- */
+typedef enum mtp_op { MTP_OP_DRAFT = 0, MTP_OP_VERIFY = 1, MTP_OP_ACCEPT = 2 } mtp_op;
+
+/* Bytes of device workspace an op needs.  rows = hidden rows of the call (draft: B,
+ * verify: B*(k+1)); n_vocab_rows = rows of the head it scores (draft: n_draft, verify
+ * and accept: vocab); B = requests.  The workspace holds per-block partial results and
+ * completion counters.  It must be 256-byte aligned and zero-filled once after it is
+ * allocated; every call leaves its counters at zero again, so one workspace of the
+ * largest size can serve every call on a stream.  Returns 0 for invalid arguments. */
+size_t mtp_workspace_bytes(int32_t op, int32_t rows, int32_t n_vocab_rows, int32_t B);
+
+/* ---------------------------------------------------------------------------------- */
+/* the four calls                                                                      */
+/* ---------------------------------------------------------------------------------- */
+
+/* Draft head, one draft slot for B requests (lucebox-hub PR above, section "What":
+ * a 64,000-row draft head, token picked on the GPU and fed from device memory).
+ *   z[b][x] = sum_j W[x][j] * hidden[b][j]   for x < n_draft   (fp32 accumulation)
+ *   T = 0: token = lowest-id argmax of z;  T > 0: token = argmax(z/T + Gumbel(stream 0,
+ *   row = slot)), a sample of q = softmax(z/T) over the first n_draft ids.
+ * hidden:        [B][d] in htype.
+ * draft_tokens:  int32 [B][k_max]; writes column `slot`; -1 for an all -inf row.
+ * draft_stats:   mtp_row_stats [B][k_max]; writes column `slot`.
+ * draft_logits:  float [B][k_max][n_draft] raw (unsanitised) logits, writes slot `slot`;
+ *                required when T > 0 (the residual needs q), may be NULL at T = 0.
+ * 1 <= n_draft <= vocab; 1 <= B <= 128; 0 <= slot < k_max <= 7.                       */
+int mtp_draft_head(const mtp_head* head, int32_t n_draft, const void* hidden, int32_t htype,
+                   int32_t B, int32_t slot, int32_t k_max, const mtp_sampling* smp,
+                   int32_t* draft_tokens, mtp_row_stats* draft_stats, float* draft_logits,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Verify pass: full-vocabulary logits of the k+1 verify rows of B requests in one
+ * batched pass (lucebox-hub PR above, section "What"; its "Exactness" section requires
+ * the verify to be batch-invariant: a row's logits and statistics here do not depend on
+ * B, k or the row's position in the batch).
+ * hidden:        [B][k+1][d] in htype; row 0 = the last committed token, row i = draft d_i.
+ * draft_tokens:  int32 [B][k_max]; row i < k records z at draft_tokens[b][i].
+ * row_stats:     mtp_row_stats [B][k+1].
+ * logits:        float [B][k+1][vocab] raw logits; required when T > 0, else may be NULL.
+ * 1 <= k <= k_max <= 7; 1 <= B*(k+1) <= 128.                                           */
+int mtp_verify_logits(const mtp_head* head, const void* hidden, int32_t htype, int32_t B,
+                      int32_t k, const int32_t* draft_tokens, int32_t k_max,
+                      const mtp_sampling* smp, mtp_row_stats* row_stats, float* logits,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Acceptance for B requests (one block per request).  For i = 0..k-1, draft t = d_{i+1}:
+ *   a target row i that is all -inf stops the block before it (MTP_ACC_ROW_INVALID,
+ *   n_emit = n_accept = i, no further token);
+ *   T = 0: accepted iff t == argmax of verify row i (lucebox-hub PR, "Exactness");
+ *   T > 0: accepted iff p_i(t) > 0 and u*q_i(t) <= p_i(t), u from stream 1 (DS4Server
+ *          issue, closing comment "Review"); q is 0 outside the draft vocabulary;
+ *   at the first rejection the next token is y_i (T = 0) or a draw from
+ *   max(0, p_i - q_i) renormalised (Gumbel-max on stream 2, row i); an empty residual
+ *   draws from p_i instead (MTP_ACC_RESID_FALLBACK);
+ *   an accepted t == eos_id ends the block with EOS as its last token (DS4Server issue,
+ *   "Implementation": nothing is kept beyond EOS); n_accept = i;
+ *   all k accepted: a bonus token from row k (argmax, or the stream-2 sample).
+ * Inputs are the outputs of the draft and verify calls of the same cycle (draft_logits
+ * and logits are read only when T > 0).  vocab and n_draft must match those calls.
+ * out_tokens: int32 [B][k+1] = d_1..d_a, last, then -1;  n_accept, n_emit: int32 [B]
+ * (n_emit = n_accept + 1 except with MTP_ACC_ROW_INVALID);  flags: uint32 [B].        */
+int mtp_accept_sample(int32_t B, int32_t k, int32_t k_max, int32_t vocab, int32_t n_draft,
+                      const mtp_sampling* smp, const int32_t* draft_tokens,
+                      const mtp_row_stats* draft_stats, const float* draft_logits,
+                      const mtp_row_stats* row_stats, const float* logits,
+                      int32_t* out_tokens, int32_t* n_accept, int32_t* n_emit, uint32_t* flags,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Commit (DS4Server issue, "Implementation": commit only accepted rows, trim rejected
+ * rows; lucebox-hub PR, "Exactness": state restored bit-exactly).  Per request b with
+ * a = clamp(n_accept[b], 0, k) and L = clamp(kv_len[b], 0, max_rows):
+ *   live[b] <- snapshots[b][a]                        (state_bytes bytes, a byte copy)
+ *   rows L+a+1 .. L+k of every layer's K and V in kv  are zero-filled (clipped to max_rows)
+ *   kv_len[b] <- min(L + a + 1, max_rows)
+ * snapshots: [B][k+1][state_bytes], snapshot r = recurrent state after verify row r.
+ * live:      [B][state_bytes].
+ * kv:        [B][n_layers][2][max_rows][kv_row_bytes] (may be NULL when n_layers = 0).
+ * state_bytes and kv_row_bytes must be multiples of 16.                               */
+int mtp_commit_state(int32_t B, int32_t k, const int32_t* n_accept, const void* snapshots,
+                     void* live, size_t state_bytes, void* kv, int32_t n_layers,
+                     int32_t max_rows, size_t kv_row_bytes, int32_t* kv_len, void* stream);
+
+/* ---------------------------------------------------------------------------------- */
+/* misc                                                                                */
+/* ---------------------------------------------------------------------------------- */
+const char* mtp_status_str(int status);   /* static string; never NULL                 */
+int mtp_abi_version(void);                /* MTP_ABI_VERSION                            */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTP_H_ */

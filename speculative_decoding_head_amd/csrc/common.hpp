@@ -1,0 +1,167 @@
+// Device-side building blocks shared by the LM-head, acceptance and commit kernels:
+// MFMA operand types, Philox4x32-10, Gumbel / uniform maps, and the running row
+// statistics merged by the fused LM-head epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mtp.h"
+
+namespace mtp {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kPosInf = __builtin_huge_valf();
+constexpr int kNoIndex = 0x7fffffff;
+
+// Philox stream ids (the counter's second word is stream << 8 | row).
+constexpr uint32_t kStreamDraft = 0;
+constexpr uint32_t kStreamAccept = 1;
+constexpr uint32_t kStreamResample = 2;
+
+// ---------------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32->64
+// multiplies on counter words 0 and 2, whose high halves are crossed with words 1 and 3
+// and the round key; the key is bumped by the two Weyl increments between rounds.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c.x;
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo1 = 0xCD9E8D57u * c.z;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z);
+    c = u32x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// word x & 3 of counter (x >> 2, stream << 8 | row, request, cycle)
+__device__ __forceinline__ uint32_t philox_word(uint32_t k0, uint32_t k1, uint32_t stream,
+                                                uint32_t row, uint32_t request, uint32_t cycle,
+                                                uint32_t x) {
+  const u32x4 w = philox4x32_10(u32x4{x >> 2, (stream << 8) | row, request, cycle}, k0, k1);
+  const uint32_t s = x & 3u;
+  return s == 0 ? w.x : (s == 1 ? w.y : (s == 2 ? w.z : w.w));
+}
+
+// Standard Gumbel noise -ln(-ln u), u = (2 (w >> 9) + 1) 2^-24.  -ln u is taken as
+// -log1p(-(1 - u)) with 1 - u formed exactly from the integer, so draws near u = 1
+// (the ones that win an argmax over many ids) keep full relative precision.
+__device__ __forceinline__ float gumbel_from_word(uint32_t w) {
+  const uint32_t m = w >> 9;
+  const float one_minus_u = static_cast<float>(16777215u - 2u * m) * 5.9604644775390625e-8f;
+  const float neg_ln_u = -log1pf(-one_minus_u);
+  return -logf(neg_ln_u);
+}
+
+// acceptance uniform u = ((w >> 8) + 1) 2^-24 in (0, 1]
+__device__ __forceinline__ float uniform_accept(uint32_t w) {
+  return static_cast<float>((w >> 8) + 1u) * 5.9604644775390625e-8f;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Sanitised logit given the row's flags: NaN -> -inf; in a row holding +inf, +inf -> 0
+// and everything else -> -inf.
+__device__ __forceinline__ float sanitize(float z, uint32_t row_flags) {
+  if (row_flags & MTP_ROW_POSINF) return z == kPosInf ? 0.0f : kNegInf;
+  return (z != z) ? kNegInf : z;
+}
+
+// ---------------------------------------------------------------------------------
+// Running statistics of one hidden row over a set of vocabulary rows.  Within one
+// lane ids are pushed in increasing order, so a strict '>' keeps the lowest id on ties;
+// merges compare ids explicitly.  48 bytes.
+// ---------------------------------------------------------------------------------
+struct RowAcc {
+  float m;        // max of finite z / T_eff (-inf if none yet)
+  float s;        // sum of exp(z / T_eff - m) over finite z
+  float zmax;     // max finite z
+  int imax;       // its lowest id (kNoIndex if none)
+  float gbest;    // best z / T + Gumbel over finite z
+  int gidx;       // its id
+  float gz;       // z at gidx
+  int nonfinite;  // count of NaN / +-inf
+  int nposinf;    // count of +inf
+  int pinf_min;   // lowest +inf id
+  float pg;       // best Gumbel among +inf ids (their sanitised logit is 0)
+  int pgidx;
+};
+
+__device__ __forceinline__ void rowacc_init(RowAcc& a) {
+  a.m = kNegInf; a.s = 0.0f; a.zmax = kNegInf; a.imax = kNoIndex;
+  a.gbest = kNegInf; a.gidx = kNoIndex; a.gz = kNegInf;
+  a.nonfinite = 0; a.nposinf = 0; a.pinf_min = kNoIndex; a.pg = kNegInf; a.pgidx = kNoIndex;
+}
+
+template <bool SAMPLED>
+__device__ __forceinline__ void rowacc_push(RowAcc& a, float z, int x, float inv_t, float gumbel) {
+  if (__builtin_isfinite(z)) {
+    if (z > a.zmax) { a.zmax = z; a.imax = x; }
+    const float sv = z * inv_t;
+    if (sv > a.m) {
+      a.s = a.s * __expf(a.m - sv) + 1.0f;
+      a.m = sv;
+    } else {
+      a.s += __expf(sv - a.m);
+    }
+    if (SAMPLED) {
+      const float sc = sv + gumbel;
+      if (sc > a.gbest) { a.gbest = sc; a.gidx = x; a.gz = z; }
+    }
+  } else {
+    a.nonfinite += 1;
+    if (z > 0.0f) {
+      a.nposinf += 1;
+      a.pinf_min = min(a.pinf_min, x);
+      if (SAMPLED && gumbel > a.pg) { a.pg = gumbel; a.pgidx = x; }
+    }
+  }
+}
+
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// a <- merge(a, b).  Commutative: merge(a, b) and merge(b, a) give the same bits.
+__device__ __forceinline__ void rowacc_merge(RowAcc& a, const RowAcc& b) {
+  const float m = fmaxf(a.m, b.m);
+  const float sa = (a.m == kNegInf) ? 0.0f : a.s * __expf(a.m - m);
+  const float sb = (b.m == kNegInf) ? 0.0f : b.s * __expf(b.m - m);
+  a.m = m;
+  a.s = sa + sb;
+  if (better(b.zmax, b.imax, a.zmax, a.imax)) { a.zmax = b.zmax; a.imax = b.imax; }
+  if (better(b.gbest, b.gidx, a.gbest, a.gidx)) { a.gbest = b.gbest; a.gidx = b.gidx; a.gz = b.gz; }
+  a.nonfinite += b.nonfinite;
+  a.nposinf += b.nposinf;
+  a.pinf_min = min(a.pinf_min, b.pinf_min);
+  if (better(b.pg, b.pgidx, a.pg, a.pgidx)) { a.pg = b.pg; a.pgidx = b.pgidx; }
+}
+
+__device__ __forceinline__ RowAcc rowacc_shfl_xor(const RowAcc& a, int mask) {
+  RowAcc b;
+  b.m = __shfl_xor(a.m, mask);
+  b.s = __shfl_xor(a.s, mask);
+  b.zmax = __shfl_xor(a.zmax, mask);
+  b.imax = __shfl_xor(a.imax, mask);
+  b.gbest = __shfl_xor(a.gbest, mask);
+  b.gidx = __shfl_xor(a.gidx, mask);
+  b.gz = __shfl_xor(a.gz, mask);
+  b.nonfinite = __shfl_xor(a.nonfinite, mask);
+  b.nposinf = __shfl_xor(a.nposinf, mask);
+  b.pinf_min = __shfl_xor(a.pinf_min, mask);
+  b.pg = __shfl_xor(a.pg, mask);
+  b.pgidx = __shfl_xor(a.pgidx, mask);
+  return b;
+}
+
+}  // namespace mtp

@@ -1,0 +1,88 @@
+// Host-side launch interface of the kernels behind the C ABI.  Validation happens in
+// api.cpp before any of these is called; the launchers only size grids and enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mtp.h"
+
+namespace mtp {
+
+// Blocks of the LM-head kernels for a head of n_rows vocabulary rows.  A function of
+// n_rows only, so that a row's statistics never depend on how many hidden rows share
+// the launch (batch invariance).
+int lmhead_grid(int n_rows);
+constexpr int kLmheadThreads = 256;
+constexpr int kLmheadMaxRows = 16;        // hidden rows per launch of the LM-head kernels
+constexpr size_t kPartialBytes = 48;      // sizeof(RowAcc)
+constexpr int kAcceptThreads = 256;
+int accept_slices(int vocab, float temperature);
+
+struct LmheadLaunch {
+  int wtype;
+  const void* w;
+  const uint16_t* scale;
+  const uint16_t* minv;
+  int d;
+  int n_rows;             // vocabulary rows scored (n_draft or vocab)
+  const void* hidden;     // [M][d]
+  int htype;
+  int M;                  // hidden rows
+  int rows_per_req;       // hidden rows per request (1 for the draft head, k+1 for verify)
+  int row_base;           // Philox row of hidden row 0 of a request (draft slot, or 0)
+  int stream_id;          // Philox stream (0 draft, 2 verify)
+  uint32_t key0, key1, cycle, request_base;
+  float inv_t;            // 1 / T_eff
+  int sampled;            // T > 0
+  int verify;             // 1: verify pass, 0: draft head
+  const int32_t* drafts;  // verify: [B][k_max]
+  int k_max, k;
+  int32_t* tokens;        // draft: [B][k_max], column row_base
+  mtp_row_stats* stats;   // row j -> stats[j * out_stride + out_offset]
+  int out_stride, out_offset;
+  float* logits;          // row j -> logits + j * logits_stride (NULL: not stored)
+  long long logits_stride;
+  void* ws;               // partials, drafted-logit slots, completion counter
+};
+
+size_t lmhead_ws_bytes(int M, int n_rows);
+size_t lmhead_lds_bytes_for(int wtype, int d, int M);   // LDS a launch needs
+hipError_t launch_lmhead(const LmheadLaunch& p, hipStream_t stream);
+
+struct AcceptLaunch {
+  int B, k, k_max, vocab, n_draft;
+  float temperature;
+  int eos;
+  uint32_t key0, key1, cycle, request_base;
+  const int32_t* drafts;
+  const mtp_row_stats* dstats;
+  const float* dlogits;
+  const mtp_row_stats* vstats;
+  const float* vlogits;
+  int32_t* out_tokens;
+  int32_t* n_accept;
+  int32_t* n_emit;
+  uint32_t* flags;
+  void* ws;
+};
+
+size_t accept_ws_bytes(int B, int vocab, float temperature);
+hipError_t launch_accept(const AcceptLaunch& p, hipStream_t stream);
+
+struct CommitLaunch {
+  int B, k;
+  const int32_t* n_accept;
+  const void* snapshots;
+  void* live;
+  size_t state_bytes;
+  void* kv;
+  int n_layers, max_rows;
+  size_t kv_row_bytes;
+  int32_t* kv_len;
+};
+
+hipError_t launch_commit(const CommitLaunch& p, hipStream_t stream);
+
+}  // namespace mtp

@@ -1,0 +1,215 @@
+"""Thin Python binding of libmtp.so (argument marshalling only).
+
+Every step of the cycle runs in the HIP kernels behind the C ABI; this module checks
+tensors (device, dtype, contiguity, 16-byte alignment), passes raw device pointers and
+the current HIP stream, and maps status codes to exceptions.  PyTorch supplies device
+memory and streams only.  There is no CPU fallback: without the built library every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmtp.so")
+
+# mirrors of include/mtp.h
+MTP_OK = 0
+W_F32, W_BF16, W_Q4A32 = 0, 1, 2
+H_F32, H_BF16 = 0, 1
+OP_DRAFT, OP_VERIFY, OP_ACCEPT = 0, 1, 2
+ROW_NONFINITE, ROW_POSINF, ROW_INVALID = 0x1, 0x2, 0x4
+ACC_ALL_ACCEPTED, ACC_EOS, ACC_RESID_FALLBACK, ACC_ROW_INVALID = 0x01, 0x02, 0x04, 0x08
+ACC_NONFINITE_TARGET, ACC_NONFINITE_DRAFT, ACC_DRAFT_INVALID = 0x10, 0x20, 0x40
+ROW_STATS_WORDS = 8   # sizeof(mtp_row_stats) / 4
+
+EXPORTED = ("mtp_draft_head", "mtp_verify_logits", "mtp_accept_sample", "mtp_commit_state",
+            "mtp_workspace_bytes", "mtp_status_str", "mtp_abi_version")
+
+
+class MtpError(RuntimeError):
+    pass
+
+
+class _Head(ctypes.Structure):
+    _fields_ = [("wtype", ctypes.c_int32), ("d", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("w", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("minv", ctypes.c_void_p)]
+
+
+class _Sampling(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("eos_id", ctypes.c_int32), ("seed", ctypes.c_uint64),
+                ("cycle", ctypes.c_uint32), ("request_base", ctypes.c_uint32)]
+
+
+_lib_handle = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmtp.so (once).  Raises MtpError if it has not been built."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(path):
+        raise MtpError(f"{path} is missing: build it with `python -m speculative_decoding_head_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    hp, sp = ctypes.POINTER(_Head), ctypes.POINTER(_Sampling)
+    lib.mtp_draft_head.argtypes = [hp, i32, vp, i32, i32, i32, i32, sp, vp, vp, vp, vp, sz, vp]
+    lib.mtp_verify_logits.argtypes = [hp, vp, i32, i32, i32, vp, i32, sp, vp, vp, vp, sz, vp]
+    lib.mtp_accept_sample.argtypes = [i32, i32, i32, i32, i32, sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.mtp_commit_state.argtypes = [i32, i32, vp, vp, vp, sz, vp, i32, i32, sz, vp, vp]
+    for f in ("mtp_draft_head", "mtp_verify_logits", "mtp_accept_sample", "mtp_commit_state", "mtp_abi_version"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.mtp_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.mtp_workspace_bytes.restype = sz
+    lib.mtp_status_str.argtypes = [ctypes.c_int]
+    lib.mtp_status_str.restype = ctypes.c_char_p
+    lib.mtp_abi_version.argtypes = []
+    _lib_handle = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != MTP_OK:
+        msg = load_library().mtp_status_str(status).decode()
+        raise MtpError(f"mtp status {status}: {msg}")
+
+
+# ---------------------------------------------------------------------------------
+# tensor marshalling
+# ---------------------------------------------------------------------------------
+def _ptr(t: Optional[torch.Tensor], dtypes=None, name: str = "tensor") -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise MtpError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise MtpError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise MtpError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    p = t.data_ptr()
+    if p % 16:
+        raise MtpError(f"{name} is not 16-byte aligned")
+    return p
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _htype(h: torch.Tensor) -> int:
+    if h.dtype == torch.float32:
+        return H_F32
+    if h.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return H_BF16
+    raise MtpError(f"hidden rows must be float32 or bf16, got {h.dtype}")
+
+
+@dataclass
+class Head:
+    """Device-resident shared LM head.  w: float32 [V][d] | bf16 [V][d] | uint8 [V][d/2]."""
+    wtype: int
+    d: int
+    vocab: int
+    w: torch.Tensor
+    scale: Optional[torch.Tensor] = None
+    minv: Optional[torch.Tensor] = None
+
+    def _struct(self) -> _Head:
+        return _Head(self.wtype, self.d, self.vocab, 0, _ptr(self.w, name="w"),
+                     _ptr(self.scale, name="scale"), _ptr(self.minv, name="minv"))
+
+
+def sampling(temperature: float = 0.0, eos_id: int = -1, seed: int = 0, cycle: int = 0,
+             request_base: int = 0) -> _Sampling:
+    return _Sampling(float(temperature), int(eos_id), int(seed) & (2**64 - 1), int(cycle) & 0xFFFFFFFF,
+                     int(request_base) & 0xFFFFFFFF)
+
+
+def row_stats_empty(*shape, device="cuda") -> torch.Tensor:
+    """Storage for mtp_row_stats: int32 [..., 8]."""
+    return torch.zeros(*shape, ROW_STATS_WORDS, dtype=torch.int32, device=device)
+
+
+def row_stats_fields(t: torch.Tensor) -> dict:
+    """Split an int32 [..., 8] mtp_row_stats tensor into named fields (views)."""
+    f = t.view(torch.float32)
+    return dict(max=f[..., 0], lse=f[..., 1], z_tok=f[..., 2], argmax=t[..., 3], sample=t[..., 4],
+                flags=t[..., 5], n_posinf=t[..., 6])
+
+
+def workspace_bytes(op: int, rows: int, n_vocab_rows: int, B: int) -> int:
+    return int(load_library().mtp_workspace_bytes(op, rows, n_vocab_rows, B))
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zero-filled, 256-byte aligned workspace of at least nbytes."""
+    t = torch.zeros(max(int(nbytes), 256) + 256, dtype=torch.uint8, device=device)
+    off = (-t.data_ptr()) % 256
+    return t[off:off + max(int(nbytes), 256)]
+
+
+# ---------------------------------------------------------------------------------
+# the four calls (same names as the C ABI)
+# ---------------------------------------------------------------------------------
+def mtp_draft_head(head: Head, n_draft: int, hidden: torch.Tensor, slot: int, k_max: int, smp: _Sampling,
+                   draft_tokens: torch.Tensor, draft_stats: torch.Tensor, draft_logits: Optional[torch.Tensor],
+                   ws: torch.Tensor, stream=None) -> None:
+    lib = load_library()
+    B = hidden.shape[0]
+    h = head._struct()
+    _check(lib.mtp_draft_head(ctypes.byref(h), int(n_draft), _ptr(hidden, name="hidden"), _htype(hidden), int(B),
+                              int(slot), int(k_max), ctypes.byref(smp), _ptr(draft_tokens, (torch.int32,), "draft_tokens"),
+                              _ptr(draft_stats, (torch.int32,), "draft_stats"),
+                              _ptr(draft_logits, (torch.float32,), "draft_logits"),
+                              _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def mtp_verify_logits(head: Head, hidden: torch.Tensor, k: int, draft_tokens: torch.Tensor, k_max: int,
+                      smp: _Sampling, row_stats: torch.Tensor, logits: Optional[torch.Tensor],
+                      ws: torch.Tensor, stream=None) -> None:
+    lib = load_library()
+    B = hidden.shape[0] if hidden.dim() == 3 else hidden.shape[0] // (k + 1)
+    h = head._struct()
+    _check(lib.mtp_verify_logits(ctypes.byref(h), _ptr(hidden, name="hidden"), _htype(hidden), int(B), int(k),
+                                 _ptr(draft_tokens, (torch.int32,), "draft_tokens"), int(k_max), ctypes.byref(smp),
+                                 _ptr(row_stats, (torch.int32,), "row_stats"),
+                                 _ptr(logits, (torch.float32,), "logits"),
+                                 _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def mtp_accept_sample(B: int, k: int, k_max: int, vocab: int, n_draft: int, smp: _Sampling,
+                      draft_tokens: torch.Tensor, draft_stats: torch.Tensor, draft_logits: Optional[torch.Tensor],
+                      row_stats: torch.Tensor, logits: Optional[torch.Tensor], out_tokens: torch.Tensor,
+                      n_accept: torch.Tensor, n_emit: torch.Tensor, flags: torch.Tensor,
+                      ws: Optional[torch.Tensor], stream=None) -> None:
+    lib = load_library()
+    _check(lib.mtp_accept_sample(int(B), int(k), int(k_max), int(vocab), int(n_draft), ctypes.byref(smp),
+                                 _ptr(draft_tokens, (torch.int32,), "draft_tokens"),
+                                 _ptr(draft_stats, (torch.int32,), "draft_stats"),
+                                 _ptr(draft_logits, (torch.float32,), "draft_logits"),
+                                 _ptr(row_stats, (torch.int32,), "row_stats"),
+                                 _ptr(logits, (torch.float32,), "logits"),
+                                 _ptr(out_tokens, (torch.int32,), "out_tokens"),
+                                 _ptr(n_accept, (torch.int32,), "n_accept"), _ptr(n_emit, (torch.int32,), "n_emit"),
+                                 _ptr(flags, (torch.int32,), "flags"),
+                                 _ptr(ws, name="ws"), 0 if ws is None else ws.numel() * ws.element_size(),
+                                 _stream(stream)))
+
+
+def mtp_commit_state(B: int, k: int, n_accept: torch.Tensor, snapshots: Optional[torch.Tensor],
+                     live: Optional[torch.Tensor], state_bytes: int, kv: Optional[torch.Tensor], n_layers: int,
+                     max_rows: int, kv_row_bytes: int, kv_len: torch.Tensor, stream=None) -> None:
+    lib = load_library()
+    _check(lib.mtp_commit_state(int(B), int(k), _ptr(n_accept, (torch.int32,), "n_accept"),
+                                _ptr(snapshots, name="snapshots"), _ptr(live, name="live"), int(state_bytes),
+                                _ptr(kv, name="kv"), int(n_layers), int(max_rows), int(kv_row_bytes),
+                                _ptr(kv_len, (torch.int32,), "kv_len"), _stream(stream)))

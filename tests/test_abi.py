@@ -1,0 +1,164 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header declares,
+and rejects invalid arguments with the documented status codes before touching a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mtp.h")
+
+mtp = pytest.importorskip("speculative_decoding_head_amd")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mtp_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mtp.LIB_PATH):
+        pytest.skip("libmtp.so not built")
+    return mtp.load_library()
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for f in ("mtp_draft_head", "mtp_verify_logits", "mtp_accept_sample", "mtp_commit_state",
+              "mtp_workspace_bytes", "mtp_status_str", "mtp_abi_version"):
+        assert f in names
+    assert set(names) == set(mtp.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", mtp.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mtp_abi_version() == 1
+    for code in range(-7, 1):
+        s = lib.mtp_status_str(code)
+        assert s and s != b"unknown status"
+    assert lib.mtp_status_str(-99) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    draft = mtp.workspace_bytes(mtp.OP_DRAFT, 1, 64000, 1)
+    verify = mtp.workspace_bytes(mtp.OP_VERIFY, 8, 152064, 1)
+    assert draft > 256 and verify > draft
+    assert mtp.workspace_bytes(mtp.OP_VERIFY, 17, 152064, 1) == 0      # more rows than one launch takes
+    assert mtp.workspace_bytes(mtp.OP_DRAFT, 0, 10, 1) == 0
+    assert mtp.workspace_bytes(99, 1, 10, 1) == 0
+    assert mtp.workspace_bytes(mtp.OP_ACCEPT, 0, 152064, 16) > 0
+
+
+def _head(wtype=mtp.W_BF16, d=256, vocab=1024, w=0x1000, scale=None, minv=None, reserved=0):
+    return mtp.mtp._Head(wtype, d, vocab, reserved, w, scale, minv)
+
+
+FAKE = 0x10000   # never dereferenced: every case below fails validation first
+
+
+@pytest.fixture(autouse=True)
+def _no_device_launch_with_fake_pointers(request):
+    # the invalid-argument cases pass fake device pointers; they are host-logic checks and
+    # must never get near a real device, so they only run where no GPU is visible
+    if request.node.name.startswith("test_") and "rejects" in request.node.name:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("invalid-argument checks with fake pointers run on CPU-only hosts")
+
+
+@pytest.mark.parametrize("case,want", [
+    (dict(head=None), -1),
+    (dict(head=_head(w=None)), -1),
+    (dict(head=_head(wtype=7)), -3),
+    (dict(head=_head(wtype=mtp.W_F32)), -3),                     # f32 weights with bf16 hidden
+    (dict(head=_head(d=250)), -2),
+    (dict(head=_head(vocab=0)), -2),
+    (dict(head=_head(reserved=1)), -4),
+    (dict(head=_head(wtype=mtp.W_Q4A32)), -1),                   # missing scale / min
+    (dict(head=_head(wtype=mtp.W_Q4A32, d=288, scale=FAKE, minv=FAKE)), -2),
+    (dict(n_draft=2000), -2),
+    (dict(n_draft=0), -2),
+    (dict(B=17), -2),
+    (dict(slot=3, k_max=3), -4),
+    (dict(k_max=8), -2),
+    (dict(temperature=-1.0), -4),
+    (dict(temperature=float("nan")), -4),
+    (dict(temperature=1.0, logits=None), -1),
+    (dict(hidden=FAKE + 4), -5),
+    (dict(ws=None), -6),
+    (dict(ws=FAKE + 16), -5),
+    (dict(ws_bytes=8), -6),
+])
+def test_draft_head_rejects_bad_arguments(lib, case, want):
+    a = dict(head=_head(), n_draft=512, hidden=FAKE, htype=mtp.H_BF16, B=1, slot=0, k_max=3, temperature=0.0,
+             tokens=FAKE, stats=FAKE, logits=FAKE, ws=FAKE, ws_bytes=1 << 20)
+    a.update(case)
+    smp = mtp.sampling(a["temperature"])
+    head = a["head"]
+    r = lib.mtp_draft_head(ctypes.byref(head) if head is not None else None, a["n_draft"], a["hidden"], a["htype"],
+                           a["B"], a["slot"], a["k_max"], ctypes.byref(smp), a["tokens"], a["stats"], a["logits"],
+                           a["ws"], a["ws_bytes"], None)
+    assert r == want
+
+
+@pytest.mark.parametrize("case,want", [
+    (dict(k=0), -2), (dict(k=8, k_max=8), -2), (dict(k=4, k_max=3), -2),
+    (dict(B=3, k=7, k_max=7), -2),                               # 24 rows > 16 per launch
+    (dict(drafts=None), -1), (dict(stats=None), -1),
+    (dict(ws_bytes=1000), -6),
+])
+def test_verify_rejects_bad_arguments(lib, case, want):
+    a = dict(B=1, k=3, k_max=3, drafts=FAKE, stats=FAKE, ws_bytes=1 << 24)
+    a.update(case)
+    smp = mtp.sampling(0.0)
+    head = _head()
+    r = lib.mtp_verify_logits(ctypes.byref(head), FAKE, mtp.H_BF16, a["B"], a["k"], a["drafts"], a["k_max"],
+                              ctypes.byref(smp), a["stats"], None, FAKE, a["ws_bytes"], None)
+    assert r == want
+
+
+@pytest.mark.parametrize("case,want", [
+    (dict(B=0), -2), (dict(k=0), -2), (dict(n_draft=200000), -2), (dict(vocab=0), -2),
+    (dict(out=None), -1), (dict(temperature=1.0, logits=None), -1),
+    (dict(temperature=1.0, ws=None), -6),
+    (dict(temperature=1.0, ws_bytes=10), -6),
+])
+def test_accept_rejects_bad_arguments(lib, case, want):
+    a = dict(B=1, k=3, k_max=3, vocab=152064, n_draft=64000, out=FAKE, logits=FAKE, temperature=0.0, ws=FAKE,
+             ws_bytes=1 << 20)
+    a.update(case)
+    smp = mtp.sampling(a["temperature"])
+    r = lib.mtp_accept_sample(a["B"], a["k"], a["k_max"], a["vocab"], a["n_draft"], ctypes.byref(smp), FAKE, FAKE,
+                              FAKE, FAKE, a["logits"], a["out"], FAKE, FAKE, FAKE, a["ws"], a["ws_bytes"], None)
+    assert r == want
+
+
+@pytest.mark.parametrize("case,want", [
+    (dict(B=0), -2), (dict(k=8), -2), (dict(n_accept=None), -1), (dict(state_bytes=24), -2),
+    (dict(snapshots=None), -1), (dict(kv=None), -1), (dict(kv_row_bytes=12), -2), (dict(kv=FAKE + 8), -5),
+])
+def test_commit_rejects_bad_arguments(lib, case, want):
+    a = dict(B=1, k=3, n_accept=FAKE, snapshots=FAKE, state_bytes=64, kv=FAKE, kv_row_bytes=32)
+    a.update(case)
+    r = lib.mtp_commit_state(a["B"], a["k"], a["n_accept"], a["snapshots"], FAKE, a["state_bytes"], a["kv"], 2, 8,
+                             a["kv_row_bytes"], FAKE, None)
+    assert r == want
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    if not os.path.exists(mtp.LIB_PATH):
+        pytest.skip("libmtp.so not built")
+    with pytest.raises(mtp.MtpError):
+        mtp.mtp._ptr(torch.zeros(4), name="x")
