@@ -44,7 +44,57 @@ def parse():
     ap.add_argument("--cpu-cycles", type=int, default=0, help="oracle cycles for the CPU baseline (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-commit", action="store_true", help="leave the commit out of the step")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy (the HBM counter reference)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30
+
+
+def summarize_counters(fetch_csv: str, write_csv: str) -> None:
+    """Per-kernel HBM bytes per launch from rocprofv3 counter CSVs, scaled by the counters
+    of a plain copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES) in the same run."""
+    import csv
+    from collections import defaultdict
+
+    def load(path, counter):
+        per = defaultdict(list)
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                per[row["Kernel_Name"]].append(float(row["Counter_Value"]) * 1024.0)   # KiB -> B
+        return per
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+
+    def copy_kernel(per):
+        cands = [k for k in per if "copyBuffer" in k or "direct_copy" in k or "elementwise" in k and "copy" in k]
+        best = max(cands, key=lambda k: max(per[k]))
+        return max(per[best])
+
+    f_scale = COPY_BYTES / copy_kernel(fetch)
+    w_scale = COPY_BYTES / copy_kernel(write)
+    out = {"source_digest": source_digest(), "copy_bytes": COPY_BYTES,
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
+    for name in fetch:
+        short = None
+        for key in ("mtp_draft_head_kernel", "mtp_verify_logits_kernel", "mtp_accept_sample_kernel",
+                    "mtp_commit_state_kernel"):
+            if key in name:
+                short = key
+        if short is None or short in out["kernels"]:
+            continue
+        fb = float(np.median(fetch[name])) * f_scale
+        wb = float(np.median(write.get(name, [0.0]))) * w_scale
+        out["kernels"][short] = {"fetch_bytes": int(fb), "write_bytes": int(wb), "bytes_per_launch": int(fb + wb),
+                                 "launches": len(fetch[name]), "raw_kernel_name": name}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def source_digest() -> str:
@@ -67,6 +117,9 @@ def load_traffic(kernel: str, units_per_launch: float):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1", "n_gpus": args.gpus}))
@@ -142,6 +195,14 @@ def main():
                                  kv_len, stream)
             if events is not None:
                 events[k + 3].record(stream)
+
+    if args.calibrate_copy:
+        a = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     for c in range(args.warmup):
         cycle(c)

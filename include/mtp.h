@@ -80,7 +80,8 @@ typedef enum mtp_htype {
 } mtp_htype;
 
 /* Supported pairings: F32 weights with F32 hiddens; BF16 or Q4A32 weights with BF16
- * hiddens.  d must be a positive multiple of 32; vocab >= 1. */
+ * hiddens.  d must be a positive multiple of 32 (of 256 for Q4A32); vocab >= 1; the
+ * weight array of one head must be smaller than 2 GiB. */
 typedef struct mtp_head {
   int32_t wtype;       /* mtp_wtype                                                    */
   int32_t d;           /* hidden size                                                  */

@@ -175,22 +175,21 @@ __global__ __launch_bounds__(kAcceptThreads) void mtp_accept_sample_kernel(Accep
         if (better(s_score[w], s_idx[w], bs, bi)) { bs = s_score[w]; bi = s_idx[w]; }
         bm |= s_mass[w];
       }
-      part[(size_t)b * S + slice] = SlicePartial{bs, bi, bm, 0};
-      __threadfence();
-      s_last = (atomicAdd(&counters[b], 1u) == (unsigned)S - 1);
+      store_coherent_obj(&part[(size_t)b * S + slice], SlicePartial{bs, bi, bm, 0});
+      wait_stores();
+      s_last = (take_ticket(&counters[b]) == (unsigned)S - 1);
     }
     __syncthreads();
     if (!s_last) return;
     if (tid != 0) return;
-    __threadfence();
     float bs = kNegInf;
     int bi = kNoIndex, bm = 0;
     for (int sl = 0; sl < S; ++sl) {
-      const SlicePartial q = part[(size_t)b * S + sl];
+      const SlicePartial q = load_coherent_obj(&part[(size_t)b * S + sl]);
       if (better(q.score, q.idx, bs, bi)) { bs = q.score; bi = q.idx; }
       bm |= q.has_mass;
     }
-    counters[b] = 0u;
+    store_coherent(&counters[b], 0u);
     best = bs; best_idx = bi; mass = bm;
   } else {
     if (tid != 0) return;

@@ -31,6 +31,9 @@ int check_head(const mtp_head* h, int htype) {
     if (!aligned16(h->scale) || !aligned16(h->minv)) return MTP_ERR_ALIGN;
   }
   if (!aligned16(h->w)) return MTP_ERR_ALIGN;
+  // weights are addressed with 32-bit buffer offsets: at most 2 GiB per head
+  const size_t row = h->wtype == MTP_W_F32 ? (size_t)h->d * 4 : (h->wtype == MTP_W_BF16 ? (size_t)h->d * 2 : (size_t)h->d / 2);
+  if ((size_t)h->vocab * row >= ((size_t)1 << 31)) return MTP_ERR_SHAPE;
   return MTP_OK;
 }
 

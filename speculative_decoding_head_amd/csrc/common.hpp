@@ -147,6 +147,46 @@ __device__ __forceinline__ void rowacc_merge(RowAcc& a, const RowAcc& b) {
   if (better(b.pg, b.pgidx, a.pg, a.pgidx)) { a.pg = b.pg; a.pgidx = b.pgidx; }
 }
 
+// ---------------------------------------------------------------------------------
+// Data handed from one block to another inside a launch (per-block partials, the
+// drafted-token logit) is written and read with relaxed device-scope atomics: on gfx950
+// they are ordinary stores and loads carrying the device scope bits, written through to
+// and read from the point of coherence shared by all XCDs.  A device-scope fence would
+// instead write back and invalidate the whole L2 of the XCD under every other wave's
+// weight stream.  Ordering: each wave waits for its stores to be acknowledged
+// (wait_stores) before the block barrier that precedes the completion ticket.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_coherent(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ void store_coherent_obj(T* dst, const T& v) {
+  static_assert(sizeof(T) % 4 == 0, "word-sized objects only");
+  const uint32_t* s = reinterpret_cast<const uint32_t*>(&v);
+  uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) store_coherent(d + i, s[i]);
+}
+template <class T>
+__device__ __forceinline__ T load_coherent_obj(const T* src) {
+  static_assert(sizeof(T) % 4 == 0, "word-sized objects only");
+  T v;
+  uint32_t* d = reinterpret_cast<uint32_t*>(&v);
+  const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) d[i] = load_coherent(s + i);
+  return v;
+}
+// wait until this wave's memory operations (the coherent stores above) are acknowledged
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
+// completion ticket: returns the number of blocks that arrived before this one
+__device__ __forceinline__ unsigned int take_ticket(unsigned int* counter) {
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ RowAcc rowacc_shfl_xor(const RowAcc& a, int mask) {
   RowAcc b;
   b.m = __shfl_xor(a.m, mask);

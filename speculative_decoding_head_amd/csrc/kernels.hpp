@@ -14,7 +14,7 @@ namespace mtp {
 // n_rows only, so that a row's statistics never depend on how many hidden rows share
 // the launch (batch invariance).
 int lmhead_grid(int n_rows);
-constexpr int kLmheadThreads = 256;
+constexpr int kLmheadThreads = 512;
 constexpr int kLmheadMaxRows = 16;        // hidden rows per launch of the LM-head kernels
 constexpr size_t kPartialBytes = 48;      // sizeof(RowAcc)
 constexpr int kAcceptThreads = 256;

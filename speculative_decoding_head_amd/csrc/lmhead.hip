@@ -24,6 +24,8 @@
 //     argmax; then a 16-lane butterfly, a cross-wave merge through LDS, one partial per
 //     block, and the last block to finish (atomic ticket) merges the partials in block
 //     order.  No floating-point atomics: results are deterministic.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -31,12 +33,41 @@ namespace mtp {
 
 namespace {
 
+// Tuning knobs (compile-time): tiles per wave pass, K steps per prefetch chunk, the grid
+// cap, and the waves per SIMD the register budget is sized for.
+#ifndef MTP_LM_TV
+#define MTP_LM_TV 2
+#endif
+#ifndef MTP_LM_U
+#define MTP_LM_U 8
+#endif
+#ifndef MTP_LM_MAX_GRID
+#define MTP_LM_MAX_GRID 256
+#endif
+#ifndef MTP_LM_WAVES_PER_EU
+#define MTP_LM_WAVES_PER_EU 1
+#endif
+
 constexpr int kWaves = kLmheadThreads / 64;
-constexpr int TV = 2;   // 16-row vocabulary tiles per wave per pass
-constexpr int U = 8;    // K steps per prefetch chunk
-constexpr int kMaxGrid = 512;
+constexpr int TV = MTP_LM_TV;   // 16-row vocabulary tiles per wave per pass
+constexpr int U = MTP_LM_U;     // K steps per prefetch chunk
+constexpr int kMaxGrid = MTP_LM_MAX_GRID;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Raw buffer loads: a load whose byte offset lies at or beyond the record count returns
+// zeros without touching memory, so masked tiles and rows past the vocabulary need no
+// branch (a branch around a load keeps the compiler from counting outstanding loads).
+constexpr uint32_t kOOB = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
 
 // eight 4-bit codes (element 2m in the low nibble of byte m) -> bf16 values 128 + q, in
 // the lane order [q0, q2, q1, q3, q4, q6, q5, q7]
@@ -58,13 +89,32 @@ __device__ __forceinline__ size_t row_bytes(int d) {
   return WT == MTP_W_F32 ? (size_t)d * 4 : (WT == MTP_W_BF16 ? (size_t)d * 2 : (size_t)d / 2);
 }
 
+// partials are handed between blocks as three 16-byte device-scope buffer stores/loads
+constexpr int kCoherent = 16;   // cache-policy bits: device scope (sc1)
+__device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t r, uint32_t off, const RowAcc& a) {
+  const u32x4* v = reinterpret_cast<const u32x4*>(&a);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) __builtin_amdgcn_raw_buffer_store_b128(v[i], r, (int)(off + 16 * i), 0, kCoherent);
+}
+__device__ __forceinline__ RowAcc load_partial(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  RowAcc a;
+  u32x4* v = reinterpret_cast<u32x4*>(&a);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16 * i), 0, kCoherent);
+  return a;
+}
+
 template <int WT, bool SAMPLED, bool VERIFY>
 __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
+  static_assert(sizeof(RowAcc) == 48, "partials are three 16-byte vectors");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int xi = lane & 15, g = lane >> 4;
   const int M = p.M, d = p.d;
   const int nsteps = (WT == MTP_W_F32) ? d / 16 : d / 32;
+  // chunks per tile group, rounded up to even for the two-buffer pipeline (a chunk past
+  // the end reads out of range, i.e. zeros, and its MFMAs add +0)
+  const int nchunks = ((nsteps + U - 1) / U + 1) & ~1;
 
   uint4* frag = reinterpret_cast<uint4*>(smem);
   const size_t frag_bytes = (size_t)nsteps * 4 * M * 16;
@@ -72,6 +122,104 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   const size_t htab_bytes = (WT == MTP_W_Q4A32) ? (size_t)nsteps * 16 * 4 : 0;
   RowAcc* red = reinterpret_cast<RowAcc*>(smem + frag_bytes + htab_bytes);
   int* last_flag = reinterpret_cast<int*>(red + kWaves * 16);
+
+  // ---- this wave's contiguous range of 16-row tiles ------------------------------
+  const int tiles = (p.n_rows + 15) >> 4;
+  const long long nw = (long long)gridDim.x * kWaves;
+  const long long gw = (long long)blockIdx.x * kWaves + wave;
+  const int t_begin = (int)(gw * tiles / nw), t_end = (int)((gw + 1) * tiles / nw);
+
+  const unsigned char* wbase = static_cast<const unsigned char*>(p.w);
+  const size_t rb = row_bytes<WT>(d);
+  const int G32 = d / 32;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)((size_t)p.n_rows * rb));
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.scale, (uint32_t)((size_t)p.n_rows * G32 * 2));
+  const __amdgpu_buffer_rsrc_t mr = make_rsrc(p.minv, (uint32_t)((size_t)p.n_rows * G32 * 2));
+
+  // byte offsets of the lane's weight rows in tile group tb (kOOB: reads zeros)
+  auto row_offsets = [&](int tb, uint32_t (&roff)[TV]) {
+#pragma unroll
+    for (int t = 0; t < TV; ++t) {
+      const int x = (tb + t) * 16 + xi;
+      roff[t] = ((tb + t) < t_end && x < p.n_rows) ? (uint32_t)((size_t)x * rb) : kOOB;
+    }
+  };
+
+  // ---- loads and MFMA steps of one chunk (U K-steps of TV tiles) -----------------
+  // valid offsets are < 2^31 (the host caps a head at 2 GiB): OR-ing in the top bit moves a
+  // step past the end out of range without a branch, so the compiler counts loads exactly
+  typedef typename std::conditional<WT == MTP_W_Q4A32, uint32_t, uint4>::type WFrag;
+  struct Chunk {
+    WFrag w[TV][U];
+    uint4 sc[TV], mn[TV];   // 4-bit heads: scales and mins of the chunk's U groups
+  };
+  auto load = [&](Chunk& ck, const uint32_t (&roff)[TV], int s0) {
+#pragma unroll
+    for (int t = 0; t < TV; ++t) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int s = s0 + u;
+        const uint32_t oob = s < nsteps ? 0u : kOOB;
+        if constexpr (WT == MTP_W_Q4A32)
+          ck.w[t][u] = bload4(wr, (roff[t] | oob) + (uint32_t)((4 * s + g) * 4));
+        else
+          ck.w[t][u] = bload16(wr, (roff[t] | oob) + (uint32_t)((4 * s + g) * 16));
+      }
+      if constexpr (WT == MTP_W_Q4A32) {
+        const uint32_t oob = s0 < nsteps ? 0u : kOOB;
+        const uint32_t so = roff[t] == kOOB ? kOOB : (roff[t] / (uint32_t)rb) * (uint32_t)(G32 * 2);
+        ck.sc[t] = bload16(sr, (so | oob) + (uint32_t)(s0 * 2));
+        ck.mn[t] = bload16(mr, (so | oob) + (uint32_t)(s0 * 2));
+      }
+    }
+  };
+  f32x4 c[TV];
+  auto comp = [&](const Chunk& ck, int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u;
+      const uint4 a = (xi < M && s < nsteps) ? frag[(s * 4 + g) * M + xi] : uint4{0u, 0u, 0u, 0u};
+      if constexpr (WT == MTP_W_BF16) {
+#pragma unroll
+        for (int t = 0; t < TV; ++t)
+          c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(ck.w[t][u]), c[t], 0, 0, 0);
+      } else if constexpr (WT == MTP_W_F32) {
+        const float a0 = __uint_as_float(a.x), a1 = __uint_as_float(a.y);
+        const float a2 = __uint_as_float(a.z), a3 = __uint_as_float(a.w);
+#pragma unroll
+        for (int t = 0; t < TV; ++t) {
+          const uint4 w = ck.w[t][u];
+          c[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, __uint_as_float(w.x), c[t], 0, 0, 0);
+          c[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, __uint_as_float(w.y), c[t], 0, 0, 0);
+          c[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, __uint_as_float(w.z), c[t], 0, 0, 0);
+          c[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a3, __uint_as_float(w.w), c[t], 0, 0, 0);
+        }
+      } else {
+        // 4-bit affine: D = sum (128 + q) h over the group, then z += s D + (min - 128 s) sum(h)
+        if (s < nsteps) {
+          const f32x4 hs = *reinterpret_cast<const f32x4*>(htab + s * 16 + 4 * g);
+#pragma unroll
+          for (int t = 0; t < TV; ++t) {
+            const f32x4 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                as_bf16x8(a), as_bf16x8(q4_expand(ck.w[t][u])), f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            const uint32_t sw = (u < 2) ? ck.sc[t].x : (u < 4) ? ck.sc[t].y : (u < 6) ? ck.sc[t].z : ck.sc[t].w;
+            const uint32_t mw = (u < 2) ? ck.mn[t].x : (u < 4) ? ck.mn[t].y : (u < 6) ? ck.mn[t].z : ck.mn[t].w;
+            const float sv = bf16_to_f32((uint16_t)((u & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+            const float mv = bf16_to_f32((uint16_t)((u & 1) ? (mw >> 16) : (mw & 0xFFFFu)));
+            const float off = mv - 128.0f * sv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) c[t][r] = fmaf(off, hs[r], fmaf(sv, D[r], c[t][r]));
+          }
+        }
+      }
+    }
+  };
+
+  // the first chunk's weight loads are in flight while the hidden rows are staged
+  Chunk A, B;
+  uint32_t roff_cur[TV], roff_nxt[TV];
+  row_offsets(t_begin, roff_cur);
+  load(A, roff_cur, 0);
 
   // ---- stage the hidden rows as A-operand fragments -------------------------------
   const int nfrag = nsteps * 4 * M;
@@ -114,146 +262,31 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
     tok[r] = (VERIFY && rvalid[r] && i < p.k) ? p.drafts[(size_t)b * p.k_max + i] : -1;
   }
 
-  // ---- this wave's contiguous range of 16-row tiles ------------------------------
-  const int tiles = (p.n_rows + 15) >> 4;
-  const long long nw = (long long)gridDim.x * kWaves;
-  const long long gw = (long long)blockIdx.x * kWaves + wave;
-  const int t_begin = (int)(gw * tiles / nw), t_end = (int)((gw + 1) * tiles / nw);
-
-  const unsigned char* wbase = static_cast<const unsigned char*>(p.w);
-  const size_t rb = row_bytes<WT>(d);
-  const int G32 = d / 32;
-
   RowAcc acc[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) rowacc_init(acc[r]);
 
+  // ---- stream the tile groups; the next group's first chunk overlaps the epilogue --
   for (int tb = t_begin; tb < t_end; tb += TV) {
-    const unsigned char* rowp[TV];
-    bool tv[TV];
-    int xr[TV];
-#pragma unroll
-    for (int t = 0; t < TV; ++t) {
-      tv[t] = (tb + t) < t_end;
-      xr[t] = (tb + t) * 16 + xi;
-      const int xc = min(xr[t], p.n_rows - 1);
-      rowp[t] = wbase + (size_t)xc * rb;
-    }
-    f32x4 c[TV];
+    row_offsets(tb + TV, roff_nxt);
 #pragma unroll
     for (int t = 0; t < TV; ++t) c[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    if constexpr (WT == MTP_W_BF16 || WT == MTP_W_F32) {
-      uint4 bufA[TV][U], bufB[TV][U];
-      auto load = [&](uint4 (&buf)[TV][U], int s0) {
+    for (int ch = 0; ch < nchunks; ch += 2) {
+      load(B, roff_cur, (ch + 1) * U);
+      comp(A, ch * U);
+      const bool more = ch + 2 < nchunks;
+      uint32_t ro[TV];
 #pragma unroll
-        for (int t = 0; t < TV; ++t)
-          if (tv[t]) {
-            const uint4* row = reinterpret_cast<const uint4*>(rowp[t]);
-#pragma unroll
-            for (int u = 0; u < U; ++u) buf[t][u] = row[4 * (s0 + u) + g];
-          }
-      };
-      auto step = [&](const uint4 (&wv)[TV], int s) {
-        const uint4 a = (xi < M) ? frag[(s * 4 + g) * M + xi] : uint4{0u, 0u, 0u, 0u};
-        if constexpr (WT == MTP_W_BF16) {
-#pragma unroll
-          for (int t = 0; t < TV; ++t)
-            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(wv[t]), c[t], 0, 0, 0);
-        } else {
-          const float a0 = __uint_as_float(a.x), a1 = __uint_as_float(a.y);
-          const float a2 = __uint_as_float(a.z), a3 = __uint_as_float(a.w);
-#pragma unroll
-          for (int t = 0; t < TV; ++t) {
-            c[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, __uint_as_float(wv[t].x), c[t], 0, 0, 0);
-            c[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, __uint_as_float(wv[t].y), c[t], 0, 0, 0);
-            c[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, __uint_as_float(wv[t].z), c[t], 0, 0, 0);
-            c[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a3, __uint_as_float(wv[t].w), c[t], 0, 0, 0);
-          }
-        }
-      };
-      auto comp = [&](const uint4 (&buf)[TV][U], int s0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          uint4 wv[TV];
-#pragma unroll
-          for (int t = 0; t < TV; ++t) wv[t] = buf[t][u];
-          step(wv, s0 + u);
-        }
-      };
-      const int nchunks = nsteps / U;
-      if (nchunks > 0) load(bufA, 0);
-      for (int ch = 0; ch < nchunks; ch += 2) {
-        if (ch + 1 < nchunks) load(bufB, (ch + 1) * U);
-        comp(bufA, ch * U);
-        if (ch + 2 < nchunks) load(bufA, (ch + 2) * U);
-        if (ch + 1 < nchunks) comp(bufB, (ch + 1) * U);
-      }
-      for (int s = nchunks * U; s < nsteps; ++s) {
-        uint4 wv[TV];
-#pragma unroll
-        for (int t = 0; t < TV; ++t)
-          wv[t] = tv[t] ? reinterpret_cast<const uint4*>(rowp[t])[4 * s + g] : uint4{0u, 0u, 0u, 0u};
-        step(wv, s);
-      }
-    } else {
-      // 4-bit affine: U groups per chunk; scales and mins of U groups are one 16-byte load
-      uint32_t nibA[TV][U], nibB[TV][U];
-      uint4 scA[TV], mnA[TV], scB[TV], mnB[TV];
-      const uint16_t* scale_rows[TV];
-      const uint16_t* min_rows[TV];
-#pragma unroll
-      for (int t = 0; t < TV; ++t) {
-        const int xc = min(xr[t], p.n_rows - 1);
-        scale_rows[t] = p.scale + (size_t)xc * G32;
-        min_rows[t] = p.minv + (size_t)xc * G32;
-      }
-      auto load = [&](uint32_t (&nib)[TV][U], uint4 (&sc)[TV], uint4 (&mn)[TV], int s0) {
-#pragma unroll
-        for (int t = 0; t < TV; ++t)
-          if (tv[t]) {
-            const uint32_t* row = reinterpret_cast<const uint32_t*>(rowp[t]);
-#pragma unroll
-            for (int u = 0; u < U; ++u) nib[t][u] = row[4 * (s0 + u) + g];
-            sc[t] = *reinterpret_cast<const uint4*>(scale_rows[t] + s0);
-            mn[t] = *reinterpret_cast<const uint4*>(min_rows[t] + s0);
-          }
-      };
-      auto comp = [&](const uint32_t (&nib)[TV][U], const uint4 (&sc)[TV], const uint4 (&mn)[TV], int s0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int s = s0 + u;
-          const uint4 a = (xi < M) ? frag[(s * 4 + g) * M + xi] : uint4{0u, 0u, 0u, 0u};
-          const f32x4 hs = *reinterpret_cast<const f32x4*>(htab + s * 16 + 4 * g);
-#pragma unroll
-          for (int t = 0; t < TV; ++t) {
-            const f32x4 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                as_bf16x8(a), as_bf16x8(q4_expand(nib[t][u])), f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-            const uint32_t sw = (u < 2) ? sc[t].x : (u < 4) ? sc[t].y : (u < 6) ? sc[t].z : sc[t].w;
-            const uint32_t mw = (u < 2) ? mn[t].x : (u < 4) ? mn[t].y : (u < 6) ? mn[t].z : mn[t].w;
-            const float sv = bf16_to_f32((uint16_t)((u & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
-            const float mv = bf16_to_f32((uint16_t)((u & 1) ? (mw >> 16) : (mw & 0xFFFFu)));
-            const float off = mv - 128.0f * sv;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) c[t][r] = fmaf(off, hs[r], fmaf(sv, D[r], c[t][r]));
-          }
-        }
-      };
-      const int nchunks = nsteps / U;   // the host requires d % 256 == 0 for this format
-      load(nibA, scA, mnA, 0);
-      for (int ch = 0; ch < nchunks; ch += 2) {
-        if (ch + 1 < nchunks) load(nibB, scB, mnB, (ch + 1) * U);
-        comp(nibA, scA, mnA, ch * U);
-        if (ch + 2 < nchunks) load(nibA, scA, mnA, (ch + 2) * U);
-        if (ch + 1 < nchunks) comp(nibB, scB, mnB, (ch + 1) * U);
-      }
+      for (int t = 0; t < TV; ++t) ro[t] = more ? roff_cur[t] : roff_nxt[t];
+      load(A, ro, more ? (ch + 2) * U : 0);
+      comp(B, (ch + 1) * U);
     }
 
-    // ---- epilogue: this tile's logits for the lane's four hidden rows -----------
+    // epilogue: this tile group's logits for the lane's four hidden rows
 #pragma unroll
     for (int t = 0; t < TV; ++t) {
-      const int x = xr[t];
-      if (!tv[t] || x >= p.n_rows) continue;
+      const int x = (tb + t) * 16 + xi;
+      if ((tb + t) >= t_end || x >= p.n_rows) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (!rvalid[r]) continue;
@@ -267,9 +300,12 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
         }
         rowacc_push<SAMPLED>(acc[r], z, x, p.inv_t, gn);
         if (p.logits) p.logits[(long long)j * p.logits_stride + x] = z;
-        if (VERIFY && x == tok[r]) reinterpret_cast<float*>(static_cast<unsigned char*>(p.ws) + 256)[j] = z;
+        if (VERIFY && x == tok[r])
+          store_coherent(reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(p.ws) + 256) + j, __float_as_uint(z));
       }
     }
+#pragma unroll
+    for (int t = 0; t < TV; ++t) roff_cur[t] = roff_nxt[t];
   }
 
   // ---- reduce: 16 lanes of a row group, then the block's waves -------------------
@@ -291,25 +327,32 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   unsigned char* ws = static_cast<unsigned char*>(p.ws);
   unsigned int* counter = reinterpret_cast<unsigned int*>(ws);
   float* ztok = reinterpret_cast<float*>(ws + 256);
-  RowAcc* partials = reinterpret_cast<RowAcc*>(ws + 256 + ((M * 4 + 255) / 256) * 256);
+  const size_t part_off = 256 + ((size_t)(M * 4 + 255) / 256) * 256;
+  const int G = gridDim.x;
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(ws + part_off, (uint32_t)((size_t)G * M * sizeof(RowAcc)));
   if (tid < M) {
     RowAcc a = red[tid];
     for (int w = 1; w < kWaves; ++w) rowacc_merge(a, red[w * 16 + tid]);
-    partials[(size_t)blockIdx.x * M + tid] = a;
+    store_partial(pr, (uint32_t)(((size_t)blockIdx.x * M + tid) * sizeof(RowAcc)), a);
   }
-  __threadfence();
+  wait_stores();
   __syncthreads();
-  if (tid == 0) *last_flag = (atomicAdd(counter, 1u) == gridDim.x - 1);
+  if (tid == 0) *last_flag = (take_ticket(counter) == (unsigned)G - 1);
   __syncthreads();
   if (!*last_flag) return;
-  __threadfence();
 
-  // ---- last block: merge the per-block partials in block order, write results -----
-  const int G = gridDim.x;
+  // ---- last block: one wave per row merges the per-block partials in block order ---
   for (int j = wave; j < M; j += kWaves) {
-    RowAcc a;
-    rowacc_init(a);
-    for (int blk = lane; blk < G; blk += 64) rowacc_merge(a, partials[(size_t)blk * M + j]);
+    RowAcc part[kMaxGrid / 64];
+#pragma unroll
+    for (int q = 0; q < kMaxGrid / 64; ++q) {
+      const int blk = lane + 64 * q;
+      if (blk < G) part[q] = load_partial(pr, (uint32_t)(((size_t)blk * M + j) * sizeof(RowAcc)));
+      else rowacc_init(part[q]);
+    }
+    RowAcc a = part[0];
+#pragma unroll
+    for (int q = 1; q < kMaxGrid / 64; ++q) rowacc_merge(a, part[q]);
 #pragma unroll
     for (int mask = 1; mask < 64; mask <<= 1) {
       const RowAcc o = rowacc_shfl_xor(a, mask);
@@ -342,7 +385,9 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
       if (VERIFY) {
         const int b = j / p.rows_per_req, i = j % p.rows_per_req;
         const int t = (i < p.k) ? p.drafts[(size_t)b * p.k_max + i] : -1;
-        st.z_tok = (t >= 0 && t < p.n_rows && !(fl & MTP_ROW_INVALID)) ? sanitize(ztok[j], fl) : kNegInf;
+        st.z_tok = (t >= 0 && t < p.n_rows && !(fl & MTP_ROW_INVALID))
+                       ? sanitize(__uint_as_float(load_coherent(reinterpret_cast<const uint32_t*>(ztok) + j)), fl)
+                       : kNegInf;
       } else {
         st.z_tok = (fl & MTP_ROW_POSINF) ? 0.0f : ((fl & MTP_ROW_INVALID) ? kNegInf : (SAMPLED ? a.gz : a.zmax));
         p.tokens[(size_t)j * p.k_max + p.row_base] = st.sample;
@@ -350,18 +395,20 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
       p.stats[(size_t)j * p.out_stride + p.out_offset] = st;
     }
   }
-  if (tid == 0) *counter = 0u;
+  if (tid == 0) store_coherent(counter, 0u);
 }
 
 }  // namespace
 
 template <int WT, bool SAMPLED>
-__global__ __launch_bounds__(kLmheadThreads) void mtp_draft_head_kernel(LmheadLaunch p) {
+__global__ __launch_bounds__(kLmheadThreads) __attribute__((amdgpu_waves_per_eu(MTP_LM_WAVES_PER_EU)))
+void mtp_draft_head_kernel(LmheadLaunch p) {
   lmhead_body<WT, SAMPLED, false>(p);
 }
 
 template <int WT, bool SAMPLED>
-__global__ __launch_bounds__(kLmheadThreads) void mtp_verify_logits_kernel(LmheadLaunch p) {
+__global__ __launch_bounds__(kLmheadThreads) __attribute__((amdgpu_waves_per_eu(MTP_LM_WAVES_PER_EU)))
+void mtp_verify_logits_kernel(LmheadLaunch p) {
   lmhead_body<WT, SAMPLED, true>(p);
 }
 

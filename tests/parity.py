@@ -16,8 +16,10 @@ def close(a, b, tol):
     b = np.asarray(b, dtype=np.float64)
     both_ninf = (a == NEG_INF) & (b == NEG_INF)
     both_pinf = (a == np.inf) & (b == np.inf)
-    diff = np.abs(a - b)
-    return both_ninf | both_pinf | (diff <= tol)
+    both_nan = np.isnan(a) & np.isnan(b)
+    with np.errstate(invalid="ignore"):
+        diff = np.abs(a - b)
+    return both_ninf | both_pinf | both_nan | (diff <= tol)
 
 
 def check_draft_slot(gd_tok, gd_stats, od, T, delta, slot, tag=""):
