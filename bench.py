@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--cpu-cycles", type=int, default=0, help="oracle cycles for the CPU baseline (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-commit", action="store_true", help="leave the commit out of the step")
+    ap.add_argument("--row-major", action="store_true",
+                    help="keep the head row-major instead of repacking it once into the tiled layout")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (the HBM counter reference)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -146,6 +148,10 @@ def main():
         dh = mtp.Head(mtp.W_Q4A32, wl.d, wl.V, torch.from_numpy(head.w).to(dev),
                       torch.from_numpy(head.scale.view(np.int16)).to(dev),
                       torch.from_numpy(head.minv.view(np.int16)).to(dev))
+    if not args.row_major:
+        # one-time weight preparation at load: fragment-major tiles (same numbers, same logits)
+        dh = mtp.tiled_head(dh)
+        torch.cuda.synchronize()
     B, k, nd, V, d, T = wl.B, wl.k, wl.n_draft, wl.V, wl.d, wl.temperature
     hv_t = torch.from_numpy(hv.view(np.int16)).to(dev)                          # [B][k+1][d]
     hd_slots = [torch.from_numpy(np.ascontiguousarray(hd[:, i]).view(np.int16)).to(dev) for i in range(k)]
@@ -262,7 +268,8 @@ def main():
         "dtype": "bf16" if wl.wtype == "bf16" else "q4a32",
         "data": "synthetic",
         "config": {"workload": args.workload, "d": d, "V": V, "n_draft": nd, "k": k, "batch": B,
-                   "temperature": T, "weights": wl.wtype, "accumulate": "fp32",
+                   "temperature": T, "weights": wl.wtype, "layout": "row-major" if args.row_major else "tiled",
+                   "accumulate": "fp32",
                    "step": f"{k} draft-head calls + verify ({B * (k + 1)} rows) + accept"
                            + (" + commit (36 MiB snapshot select, 12-layer KV trim)" if with_commit else "")},
         "roofline": roofline,

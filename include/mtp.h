@@ -66,12 +66,25 @@ typedef enum mtp_status {
 typedef enum mtp_wtype {
   MTP_W_F32 = 0,   /* w: float [vocab][d]                                              */
   MTP_W_BF16 = 1,  /* w: bf16 bit patterns, uint16 [vocab][d]                          */
-  MTP_W_Q4A32 = 2  /* 4-bit affine, 32-value groups along d (DS4Server issue above,
+  MTP_W_Q4A32 = 2, /* 4-bit affine, 32-value groups along d (DS4Server issue above,
                       closing comment "Implementation"):  w[x][32g+j] = scale*q + min,
                       q = unsigned nibble j of group g;
                         w:     uint8 [vocab][d/2], element 2m in the low nibble of byte m,
                                element 2m+1 in the high nibble;
                         scale: bf16 [vocab][d/32];  minv: bf16 [vocab][d/32]            */
+  /* Tiled layouts: the same numbers as BF16 / Q4A32, rearranged so that the LM-head
+   * kernels read 1024 contiguous bytes per wave per load.  Rows come in tiles of 16
+   * (tile t = rows 16t..16t+15; rows past vocab are zero).  Made by mtp_pack_head.   */
+  MTP_W_BF16_TILED = 3,  /* w: block (t, s) of 1024 bytes at ((t*(d/32) + s) * 1024),
+                            s = 32-value step; bytes 16l..16l+15 of the block (l = 0..63)
+                            hold W[16t + l%16][32s + 8(l/16) + e], e = 0..7 (bf16)       */
+  MTP_W_Q4A32_TILED = 4  /* w: block (t, q) of 1024 bytes at ((t*(d/128) + q) * 1024),
+                            q = group quad (groups 4q..4q+3); bytes 16l..16l+15 are four
+                            little-endian words, word u = the 4 row-major nibble bytes
+                            [16(4q+u) + 4(l/16), +4) of row 16t + l%16;
+                            scale, minv: block (t, c) of 256 bytes at ((t*(d/256) + c) * 256),
+                            c = group octet; bytes 16r..16r+15 = the 8 bf16 values of
+                            row 16t + r for groups 8c..8c+7                              */
 } mtp_wtype;
 
 typedef enum mtp_htype {
@@ -79,9 +92,9 @@ typedef enum mtp_htype {
   MTP_H_BF16 = 1   /* hidden rows: bf16 bit patterns, uint16 [rows][d]                 */
 } mtp_htype;
 
-/* Supported pairings: F32 weights with F32 hiddens; BF16 or Q4A32 weights with BF16
- * hiddens.  d must be a positive multiple of 32 (of 256 for Q4A32); vocab >= 1; the
- * weight array of one head must be smaller than 2 GiB. */
+/* Supported pairings: F32 weights with F32 hiddens; BF16, Q4A32 and their tiled forms
+ * with BF16 hiddens.  d must be a positive multiple of 32 (of 256 for the 4-bit
+ * formats); vocab >= 1; the weight array of one head must be smaller than 2 GiB. */
 typedef struct mtp_head {
   int32_t wtype;       /* mtp_wtype                                                    */
   int32_t d;           /* hidden size                                                  */
@@ -223,6 +236,21 @@ int mtp_accept_sample(int32_t B, int32_t k, int32_t k_max, int32_t vocab, int32_
 int mtp_commit_state(int32_t B, int32_t k, const int32_t* n_accept, const void* snapshots,
                      void* live, size_t state_bytes, void* kv, int32_t n_layers,
                      int32_t max_rows, size_t kv_row_bytes, int32_t* kv_len, void* stream);
+
+/* ---------------------------------------------------------------------------------- */
+/* weight preparation                                                                  */
+/* ---------------------------------------------------------------------------------- */
+/* Bytes of one array of a tiled head for a source of type wtype (MTP_W_BF16 or
+ * MTP_W_Q4A32): part 0 = w, 1 = scale, 2 = minv (0 for a part the format lacks, or for
+ * invalid arguments). */
+size_t mtp_tiled_bytes(int32_t wtype, int32_t d, int32_t vocab, int32_t part);
+
+/* Repack a row-major BF16 or Q4A32 head into the tiled layout (MTP_W_BF16_TILED /
+ * MTP_W_Q4A32_TILED) on the device, once, at load time.  dst_* are device buffers of
+ * mtp_tiled_bytes(src->wtype, ...) bytes (dst_scale and dst_minv only for Q4A32), 16-byte
+ * aligned, not overlapping the source.  The tiled head gives the LM-head kernels the
+ * same logits, bit for bit, as the row-major head it came from. */
+int mtp_pack_head(const mtp_head* src, void* dst_w, void* dst_scale, void* dst_minv, void* stream);
 
 /* ---------------------------------------------------------------------------------- */
 /* misc                                                                                */

@@ -17,23 +17,27 @@ constexpr size_t kMaxLds = 160 * 1024 - 4096;   // gfx950: 160 KiB of LDS per CU
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
+bool is_q4(int wtype) { return wtype == MTP_W_Q4A32 || wtype == MTP_W_Q4A32_TILED; }
+bool is_tiled(int wtype) { return wtype == MTP_W_BF16_TILED || wtype == MTP_W_Q4A32_TILED; }
+
 int check_head(const mtp_head* h, int htype) {
   if (!h || !h->w) return MTP_ERR_NULL;
   if (h->reserved != 0) return MTP_ERR_RANGE;
-  if (h->wtype < MTP_W_F32 || h->wtype > MTP_W_Q4A32) return MTP_ERR_DTYPE;
+  if (h->wtype < MTP_W_F32 || h->wtype > MTP_W_Q4A32_TILED) return MTP_ERR_DTYPE;
   if (htype != MTP_H_F32 && htype != MTP_H_BF16) return MTP_ERR_DTYPE;
-  // pairings: f32 x f32, bf16 x bf16, q4a32 x bf16
+  // pairings: f32 x f32; bf16, q4a32 and their tiled forms x bf16
   if ((h->wtype == MTP_W_F32) != (htype == MTP_H_F32)) return MTP_ERR_DTYPE;
   if (h->d <= 0 || h->d % 32 != 0 || h->vocab <= 0) return MTP_ERR_SHAPE;
-  if (h->wtype == MTP_W_Q4A32) {
+  if (is_q4(h->wtype)) {
     if (!h->scale || !h->minv) return MTP_ERR_NULL;
     if (h->d % 256 != 0) return MTP_ERR_SHAPE;
     if (!aligned16(h->scale) || !aligned16(h->minv)) return MTP_ERR_ALIGN;
   }
   if (!aligned16(h->w)) return MTP_ERR_ALIGN;
   // weights are addressed with 32-bit buffer offsets: at most 2 GiB per head
-  const size_t row = h->wtype == MTP_W_F32 ? (size_t)h->d * 4 : (h->wtype == MTP_W_BF16 ? (size_t)h->d * 2 : (size_t)h->d / 2);
-  if ((size_t)h->vocab * row >= ((size_t)1 << 31)) return MTP_ERR_SHAPE;
+  const size_t row = h->wtype == MTP_W_F32 ? (size_t)h->d * 4 : (is_q4(h->wtype) ? (size_t)h->d / 2 : (size_t)h->d * 2);
+  const size_t rows = is_tiled(h->wtype) ? (size_t)(h->vocab + 15) / 16 * 16 : (size_t)h->vocab;
+  if (rows * row >= ((size_t)1 << 31)) return MTP_ERR_SHAPE;
   return MTP_OK;
 }
 
@@ -79,6 +83,29 @@ size_t mtp_workspace_bytes(int32_t op, int32_t rows, int32_t n_vocab_rows, int32
     default:
       return 0;
   }
+}
+
+size_t mtp_tiled_bytes(int32_t wtype, int32_t d, int32_t vocab, int32_t part) {
+  if ((wtype != MTP_W_BF16 && wtype != MTP_W_Q4A32) || d <= 0 || d % 32 != 0 || vocab <= 0) return 0;
+  if (wtype == MTP_W_Q4A32 && d % 256 != 0) return 0;
+  if (part < 0 || part > 2) return 0;
+  return tiled_bytes(wtype, d, vocab, part);
+}
+
+int mtp_pack_head(const mtp_head* src, void* dst_w, void* dst_scale, void* dst_minv, void* stream) {
+  if (!src) return MTP_ERR_NULL;
+  if (src->wtype != MTP_W_BF16 && src->wtype != MTP_W_Q4A32) return MTP_ERR_DTYPE;
+  int st = check_head(src, MTP_H_BF16);
+  if (st != MTP_OK) return st;
+  if (!dst_w) return MTP_ERR_NULL;
+  if (!aligned16(dst_w)) return MTP_ERR_ALIGN;
+  if (tiled_bytes(src->wtype, src->d, src->vocab, 0) >= ((size_t)1 << 31)) return MTP_ERR_SHAPE;
+  if (src->wtype == MTP_W_Q4A32) {
+    if (!dst_scale || !dst_minv) return MTP_ERR_NULL;
+    if (!aligned16(dst_scale) || !aligned16(dst_minv)) return MTP_ERR_ALIGN;
+  }
+  return launch_pack(src->wtype, src->w, src->scale, src->minv, src->d, src->vocab, dst_w, dst_scale, dst_minv,
+                     static_cast<hipStream_t>(stream)) == hipSuccess ? MTP_OK : MTP_ERR_HIP;
 }
 
 int mtp_draft_head(const mtp_head* head, int32_t n_draft, const void* hidden, int32_t htype,

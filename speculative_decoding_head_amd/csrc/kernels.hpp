@@ -85,4 +85,8 @@ struct CommitLaunch {
 
 hipError_t launch_commit(const CommitLaunch& p, hipStream_t stream);
 
+size_t tiled_bytes(int wtype, int d, int vocab, int part);   // source wtype BF16 or Q4A32
+hipError_t launch_pack(int wtype, const void* w, const void* scale, const void* minv, int d, int vocab,
+                       void* dst_w, void* dst_scale, void* dst_minv, hipStream_t stream);
+
 }  // namespace mtp

@@ -68,6 +68,17 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
+// tiled heads are read once, front to back, in whole KiB: non-temporal (streaming) hint
+constexpr int kStream = 2;   // cache-policy bits: nt
+__device__ __forceinline__ uint4 bload16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kStream));
+}
+
+template <int WT> struct Layout {
+  static constexpr bool q4 = WT == MTP_W_Q4A32 || WT == MTP_W_Q4A32_TILED;
+  static constexpr bool tiled = WT == MTP_W_BF16_TILED || WT == MTP_W_Q4A32_TILED;
+  static constexpr bool f32 = WT == MTP_W_F32;
+};
 
 // eight 4-bit codes (element 2m in the low nibble of byte m) -> bf16 values 128 + q, in
 // the lane order [q0, q2, q1, q3, q4, q6, q5, q7]
@@ -86,7 +97,7 @@ __device__ __forceinline__ uint4 q4_order(uint4 v) {
 
 template <int WT>
 __device__ __forceinline__ size_t row_bytes(int d) {
-  return WT == MTP_W_F32 ? (size_t)d * 4 : (WT == MTP_W_BF16 ? (size_t)d * 2 : (size_t)d / 2);
+  return WT == MTP_W_F32 ? (size_t)d * 4 : (Layout<WT>::q4 ? (size_t)d / 2 : (size_t)d * 2);
 }
 
 // partials are handed between blocks as three 16-byte device-scope buffer stores/loads
@@ -111,7 +122,8 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int xi = lane & 15, g = lane >> 4;
   const int M = p.M, d = p.d;
-  const int nsteps = (WT == MTP_W_F32) ? d / 16 : d / 32;
+  using L = Layout<WT>;
+  const int nsteps = L::f32 ? d / 16 : d / 32;
   // chunks per tile group, rounded up to even for the two-buffer pipeline (a chunk past
   // the end reads out of range, i.e. zeros, and its MFMAs add +0)
   const int nchunks = ((nsteps + U - 1) / U + 1) & ~1;
@@ -119,7 +131,7 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   uint4* frag = reinterpret_cast<uint4*>(smem);
   const size_t frag_bytes = (size_t)nsteps * 4 * M * 16;
   float* htab = reinterpret_cast<float*>(smem + frag_bytes);
-  const size_t htab_bytes = (WT == MTP_W_Q4A32) ? (size_t)nsteps * 16 * 4 : 0;
+  const size_t htab_bytes = L::q4 ? (size_t)nsteps * 16 * 4 : 0;
   RowAcc* red = reinterpret_cast<RowAcc*>(smem + frag_bytes + htab_bytes);
   int* last_flag = reinterpret_cast<int*>(red + kWaves * 16);
 
@@ -132,23 +144,30 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   const unsigned char* wbase = static_cast<const unsigned char*>(p.w);
   const size_t rb = row_bytes<WT>(d);
   const int G32 = d / 32;
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)((size_t)p.n_rows * rb));
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.scale, (uint32_t)((size_t)p.n_rows * G32 * 2));
-  const __amdgpu_buffer_rsrc_t mr = make_rsrc(p.minv, (uint32_t)((size_t)p.n_rows * G32 * 2));
+  // row-major heads cover n_rows rows; tiled heads whole tiles (rows past vocab are zero)
+  const size_t rows_cov = L::tiled ? (size_t)tiles * 16 : (size_t)p.n_rows;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase, (uint32_t)(rows_cov * rb));
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.scale, (uint32_t)(rows_cov * G32 * 2));
+  const __amdgpu_buffer_rsrc_t mr = make_rsrc(p.minv, (uint32_t)(rows_cov * G32 * 2));
+  const uint32_t tile_bytes = (uint32_t)(16 * rb);
 
-  // byte offsets of the lane's weight rows in tile group tb (kOOB: reads zeros)
+  // per-lane base offsets in tile group tb (kOOB: reads zeros):
+  //   row-major: the lane's weight row; tiled: the tile's first block plus the lane's 16 B
   auto row_offsets = [&](int tb, uint32_t (&roff)[TV]) {
 #pragma unroll
     for (int t = 0; t < TV; ++t) {
       const int x = (tb + t) * 16 + xi;
-      roff[t] = ((tb + t) < t_end && x < p.n_rows) ? (uint32_t)((size_t)x * rb) : kOOB;
+      if constexpr (L::tiled)
+        roff[t] = (tb + t) < t_end ? (uint32_t)(tb + t) * tile_bytes + (uint32_t)(lane * 16) : kOOB;
+      else
+        roff[t] = ((tb + t) < t_end && x < p.n_rows) ? (uint32_t)((size_t)x * rb) : kOOB;
     }
   };
 
   // ---- loads and MFMA steps of one chunk (U K-steps of TV tiles) -----------------
   // valid offsets are < 2^31 (the host caps a head at 2 GiB): OR-ing in the top bit moves a
   // step past the end out of range without a branch, so the compiler counts loads exactly
-  typedef typename std::conditional<WT == MTP_W_Q4A32, uint32_t, uint4>::type WFrag;
+  typedef typename std::conditional<L::q4, uint32_t, uint4>::type WFrag;
   struct Chunk {
     WFrag w[TV][U];
     uint4 sc[TV], mn[TV];   // 4-bit heads: scales and mins of the chunk's U groups
@@ -156,20 +175,37 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   auto load = [&](Chunk& ck, const uint32_t (&roff)[TV], int s0) {
 #pragma unroll
     for (int t = 0; t < TV; ++t) {
+      if constexpr (WT == MTP_W_Q4A32_TILED) {
+        // one KiB block per group quad: four groups' nibble words per lane
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int s = s0 + u;
-        const uint32_t oob = s < nsteps ? 0u : kOOB;
-        if constexpr (WT == MTP_W_Q4A32)
-          ck.w[t][u] = bload4(wr, (roff[t] | oob) + (uint32_t)((4 * s + g) * 4));
-        else
-          ck.w[t][u] = bload16(wr, (roff[t] | oob) + (uint32_t)((4 * s + g) * 16));
+        for (int u = 0; u < U; u += 4) {
+          const uint32_t oob = s0 + u < nsteps ? 0u : kOOB;
+          const uint4 v = bload16_stream(wr, (roff[t] | oob) + (uint32_t)((s0 + u) / 4) * 1024u);
+          ck.w[t][u] = v.x; ck.w[t][u + 1] = v.y; ck.w[t][u + 2] = v.z; ck.w[t][u + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int s = s0 + u;
+          const uint32_t oob = s < nsteps ? 0u : kOOB;
+          if constexpr (WT == MTP_W_Q4A32)
+            ck.w[t][u] = bload4(wr, (roff[t] | oob) + (uint32_t)((4 * s + g) * 4));
+          else if constexpr (WT == MTP_W_BF16_TILED)
+            ck.w[t][u] = bload16_stream(wr, (roff[t] | oob) + (uint32_t)s * 1024u);
+          else
+            ck.w[t][u] = bload16(wr, (roff[t] | oob) + (uint32_t)((4 * s + g) * 16));
+        }
       }
-      if constexpr (WT == MTP_W_Q4A32) {
+      if constexpr (L::q4) {
         const uint32_t oob = s0 < nsteps ? 0u : kOOB;
-        const uint32_t so = roff[t] == kOOB ? kOOB : (roff[t] / (uint32_t)rb) * (uint32_t)(G32 * 2);
-        ck.sc[t] = bload16(sr, (so | oob) + (uint32_t)(s0 * 2));
-        ck.mn[t] = bload16(mr, (so | oob) + (uint32_t)(s0 * 2));
+        uint32_t so;
+        if constexpr (L::tiled)   // block (tile, octet) of 256 B, 16 B per row
+          so = roff[t] == kOOB ? kOOB : (roff[t] - (uint32_t)(lane * 16)) / 8u + (uint32_t)(xi * 16);
+        else
+          so = roff[t] == kOOB ? kOOB : (roff[t] / (uint32_t)rb) * (uint32_t)(G32 * 2);
+        const uint32_t step = L::tiled ? (uint32_t)(s0 / 8) * 256u : (uint32_t)(s0 * 2);
+        ck.sc[t] = bload16(sr, (so | oob) + step);
+        ck.mn[t] = bload16(mr, (so | oob) + step);
       }
     }
   };
@@ -179,11 +215,11 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
     for (int u = 0; u < U; ++u) {
       const int s = s0 + u;
       const uint4 a = (xi < M && s < nsteps) ? frag[(s * 4 + g) * M + xi] : uint4{0u, 0u, 0u, 0u};
-      if constexpr (WT == MTP_W_BF16) {
+      if constexpr (WT == MTP_W_BF16 || WT == MTP_W_BF16_TILED) {
 #pragma unroll
         for (int t = 0; t < TV; ++t)
           c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(ck.w[t][u]), c[t], 0, 0, 0);
-      } else if constexpr (WT == MTP_W_F32) {
+      } else if constexpr (L::f32) {
         const float a0 = __uint_as_float(a.x), a1 = __uint_as_float(a.y);
         const float a2 = __uint_as_float(a.z), a3 = __uint_as_float(a.w);
 #pragma unroll
@@ -226,15 +262,15 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   for (int f = tid; f < nfrag; f += kLmheadThreads) {
     const int i = f % M, sg = f / M, gg = sg & 3, s = sg >> 2;
     uint4 v;
-    if (WT == MTP_W_F32) {
+    if (L::f32) {
       v = *reinterpret_cast<const uint4*>(static_cast<const float*>(p.hidden) + (size_t)i * d + 16 * s + 4 * gg);
     } else {
       v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.hidden) + (size_t)i * d + 32 * s + 8 * gg);
-      if (WT == MTP_W_Q4A32) v = q4_order(v);
+      if (L::q4) v = q4_order(v);
     }
     frag[f] = v;
   }
-  if (WT == MTP_W_Q4A32) {
+  if (L::q4) {
     // per 32-value group and hidden row: sum of the hidden values, in k order
     for (int e = tid; e < nsteps * 16; e += kLmheadThreads) {
       const int s = e >> 4, i = e & 15;
@@ -425,7 +461,7 @@ size_t lmhead_ws_bytes(int M, int n_rows) {
 static size_t lmhead_lds_bytes(int wtype, int d, int M) {
   const int nsteps = wtype == MTP_W_F32 ? d / 16 : d / 32;
   size_t b = (size_t)nsteps * 4 * M * 16;
-  if (wtype == MTP_W_Q4A32) b += (size_t)nsteps * 16 * 4;
+  if (wtype == MTP_W_Q4A32 || wtype == MTP_W_Q4A32_TILED) b += (size_t)nsteps * 16 * 4;
   return b + kWaves * 16 * sizeof(RowAcc) + 16;
 }
 
@@ -448,6 +484,10 @@ hipError_t launch_lmhead(const LmheadLaunch& p, hipStream_t stream) {
     case MTP_W_F32: return p.sampled ? launch_t<MTP_W_F32, true>(p, stream) : launch_t<MTP_W_F32, false>(p, stream);
     case MTP_W_BF16: return p.sampled ? launch_t<MTP_W_BF16, true>(p, stream) : launch_t<MTP_W_BF16, false>(p, stream);
     case MTP_W_Q4A32: return p.sampled ? launch_t<MTP_W_Q4A32, true>(p, stream) : launch_t<MTP_W_Q4A32, false>(p, stream);
+    case MTP_W_BF16_TILED:
+      return p.sampled ? launch_t<MTP_W_BF16_TILED, true>(p, stream) : launch_t<MTP_W_BF16_TILED, false>(p, stream);
+    case MTP_W_Q4A32_TILED:
+      return p.sampled ? launch_t<MTP_W_Q4A32_TILED, true>(p, stream) : launch_t<MTP_W_Q4A32_TILED, false>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libmtp.so")
 
 # mirrors of include/mtp.h
 MTP_OK = 0
-W_F32, W_BF16, W_Q4A32 = 0, 1, 2
+W_F32, W_BF16, W_Q4A32, W_BF16_TILED, W_Q4A32_TILED = 0, 1, 2, 3, 4
 H_F32, H_BF16 = 0, 1
 OP_DRAFT, OP_VERIFY, OP_ACCEPT = 0, 1, 2
 ROW_NONFINITE, ROW_POSINF, ROW_INVALID = 0x1, 0x2, 0x4
@@ -29,7 +29,7 @@ ACC_NONFINITE_TARGET, ACC_NONFINITE_DRAFT, ACC_DRAFT_INVALID = 0x10, 0x20, 0x40
 ROW_STATS_WORDS = 8   # sizeof(mtp_row_stats) / 4
 
 EXPORTED = ("mtp_draft_head", "mtp_verify_logits", "mtp_accept_sample", "mtp_commit_state",
-            "mtp_workspace_bytes", "mtp_status_str", "mtp_abi_version")
+            "mtp_workspace_bytes", "mtp_tiled_bytes", "mtp_pack_head", "mtp_status_str", "mtp_abi_version")
 
 
 class MtpError(RuntimeError):
@@ -68,6 +68,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, f).restype = ctypes.c_int
     lib.mtp_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.mtp_workspace_bytes.restype = sz
+    lib.mtp_tiled_bytes.argtypes = [i32, i32, i32, i32]
+    lib.mtp_tiled_bytes.restype = sz
+    lib.mtp_pack_head.argtypes = [hp, vp, vp, vp, vp]
+    lib.mtp_pack_head.restype = ctypes.c_int
     lib.mtp_status_str.argtypes = [ctypes.c_int]
     lib.mtp_status_str.restype = ctypes.c_char_p
     lib.mtp_abi_version.argtypes = []
@@ -155,6 +159,32 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     t = torch.zeros(max(int(nbytes), 256) + 256, dtype=torch.uint8, device=device)
     off = (-t.data_ptr()) % 256
     return t[off:off + max(int(nbytes), 256)]
+
+
+def mtp_tiled_bytes(wtype: int, d: int, vocab: int, part: int) -> int:
+    return int(load_library().mtp_tiled_bytes(wtype, d, vocab, part))
+
+
+def mtp_pack_head(src: Head, dst_w: torch.Tensor, dst_scale: Optional[torch.Tensor] = None,
+                  dst_minv: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Repack a row-major bf16 / 4-bit head into its tiled layout (device buffers given)."""
+    lib = load_library()
+    h = src._struct()
+    _check(lib.mtp_pack_head(ctypes.byref(h), _ptr(dst_w, name="dst_w"), _ptr(dst_scale, name="dst_scale"),
+                             _ptr(dst_minv, name="dst_minv"), _stream(stream)))
+
+
+def tiled_head(src: Head, stream=None) -> Head:
+    """Allocate device buffers and repack ``src`` into the tiled layout."""
+    if src.wtype not in (W_BF16, W_Q4A32):
+        raise MtpError("only row-major bf16 and 4-bit heads can be tiled")
+    dev = src.w.device
+    nb = [mtp_tiled_bytes(src.wtype, src.d, src.vocab, p) for p in range(3)]
+    w = torch.empty(nb[0], dtype=torch.uint8, device=dev)
+    sc = torch.empty(nb[1], dtype=torch.uint8, device=dev) if nb[1] else None
+    mn = torch.empty(nb[2], dtype=torch.uint8, device=dev) if nb[2] else None
+    mtp_pack_head(src, w, sc, mn, stream)
+    return Head(W_BF16_TILED if src.wtype == W_BF16 else W_Q4A32_TILED, src.d, src.vocab, w, sc, mn)
 
 
 # ---------------------------------------------------------------------------------

@@ -11,7 +11,16 @@ import speculative_decoding_head_amd as mtp
 WT = {"f32": mtp.W_F32, "bf16": mtp.W_BF16, "q4a32": mtp.W_Q4A32}
 
 
-def dev_head(head) -> mtp.Head:
+def dev_head(head, tiled: bool = False) -> mtp.Head:
+    """Upload a synth head; ``tiled`` repacks bf16 / 4-bit heads on the device."""
+    h = _dev_head_row_major(head)
+    if tiled:
+        h = mtp.tiled_head(h)
+        torch.cuda.synchronize()
+    return h
+
+
+def _dev_head_row_major(head) -> mtp.Head:
     if head.wtype == "f32":
         w = torch.from_numpy(np.ascontiguousarray(head.w, dtype=np.float32)).cuda()
         return mtp.Head(mtp.W_F32, head.d, head.V, w)

@@ -47,6 +47,12 @@ def bf16_model():
 
 
 @pytest.fixture(scope="module")
+def bf16_tiled(bf16_model):
+    wl, hs, head, W, dh = bf16_model
+    return wl, hs, head, W, mtp.tiled_head(dh)
+
+
+@pytest.fixture(scope="module")
 def q4_model():
     wl, rng, head = _model("q4_greedy")
     W = O.head_weights_f64(head)
@@ -143,3 +149,28 @@ def test_commit_at_model_state_size():
                                     kv_len_np, n_acc_np, k)
     assert np.array_equal(kv.cpu().numpy(), want_kv)
     assert np.array_equal(kv_len.cpu().numpy(), want_len)
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_model_tiled_head_cycle(bf16_tiled, T):
+    # the bench's head layout: tiled bf16, raw workload rows and a sampled cycle
+    wl, (hv, hd), head, W, dh = bf16_tiled
+    g, o = _run(wl, W, dh, hv, hd, T, 1234, 2)
+    check_cycle(g, o, T, DELTA, tag=f"model tiled T{T}")
+    if T > 0:
+        assert np.abs(g["logits"].astype(np.float64) - o["verify"]["logits"]).max() <= DELTA
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_q4_tiled_cycle(q4_model, T):
+    wl, _, head, W, dh = q4_model
+    th = mtp.tiled_head(dh)
+    rng = np.random.default_rng(41)
+    h_v, h_d = synth.make_hidden(rng, 2, wl.k, wl.d)
+    targets = rng.integers(3, wl.n_draft, size=(2, wl.k + 1))
+    synth.plant_rows(head, h_v, h_d, [1, 7], targets, (targets + 5) % wl.n_draft, margin=10.0)
+    hv, hd = synth.encode_hidden(h_v, "bf16"), synth.encode_hidden(h_d, "bf16")
+    g, o = _run(wl, W, th, hv, hd, T, 1234, 3)
+    check_cycle(g, o, T, DELTA, tag=f"q4 tiled T{T}")
+    if T == 0:
+        assert list(g["n_accept"]) == [1, 7]

@@ -260,3 +260,102 @@ def test_commit_every_depth_with_guards(k):
     assert np.array_equal(gl[128:-128].reshape(B, S), want_live)
     assert np.array_equal(gk[128:-128].reshape(kv.shape), want_kv)
     assert np.array_equal(d_len.cpu().numpy(), want_len)
+
+
+# ---------------------------------------------------------------------------------
+# tiled weight layouts
+# ---------------------------------------------------------------------------------
+def _tiled_bf16_reference(w_bits: np.ndarray) -> np.ndarray:
+    """The tiled bf16 layout written out from its definition in include/mtp.h."""
+    V, d = w_bits.shape
+    T = (V + 15) // 16
+    pad = np.zeros((T * 16, d), np.uint16)
+    pad[:V] = w_bits
+    out = np.zeros((T, d // 32, 64, 8), np.uint16)
+    for l in range(64):
+        rows = np.arange(T) * 16 + (l % 16)
+        for s in range(d // 32):
+            out[:, s, l, :] = pad[rows, 32 * s + 8 * (l // 16): 32 * s + 8 * (l // 16) + 8]
+    return out.reshape(-1).view(np.uint8)
+
+
+def _tiled_q4_reference(nib: np.ndarray, sc: np.ndarray, mn: np.ndarray):
+    V, half = nib.shape
+    d = half * 2
+    T = (V + 15) // 16
+    pn = np.zeros((T * 16, half), np.uint8)
+    pn[:V] = nib
+    w = np.zeros((T, d // 128, 64, 16), np.uint8)
+    for l in range(64):
+        rows = np.arange(T) * 16 + (l % 16)
+        for q in range(d // 128):
+            for u in range(4):
+                b0 = 16 * (4 * q + u) + 4 * (l // 16)
+                w[:, q, l, 4 * u:4 * u + 4] = pn[rows, b0:b0 + 4]
+
+    def tile_sc(a):
+        p = np.zeros((T * 16, d // 32), np.uint16)
+        p[:V] = a
+        o = np.zeros((T, d // 256, 16, 8), np.uint16)
+        for c in range(d // 256):
+            o[:, c, :, :] = p.reshape(T, 16, d // 32)[:, :, 8 * c:8 * c + 8]
+        return o.reshape(-1).view(np.uint8)
+    return w.reshape(-1), tile_sc(sc), tile_sc(mn)
+
+
+@pytest.mark.parametrize("wtype", ["bf16", "q4a32"])
+@pytest.mark.parametrize("V", [1013, 4096])
+def test_pack_head_matches_layout_definition(wtype, V):
+    rng = np.random.default_rng(V)
+    head = synth.make_head(rng, V, 256, wtype)
+    th = dev_head(head, tiled=True)
+    if wtype == "bf16":
+        assert np.array_equal(th.w.cpu().numpy(), _tiled_bf16_reference(head.w))
+    else:
+        w, sc, mn = _tiled_q4_reference(head.w, head.scale, head.minv)
+        assert np.array_equal(th.w.cpu().numpy(), w)
+        assert np.array_equal(th.scale.cpu().numpy(), sc)
+        assert np.array_equal(th.minv.cpu().numpy(), mn)
+
+
+@pytest.mark.parametrize("wtype", ["bf16", "q4a32"])
+@pytest.mark.parametrize("B,k", [(1, 7), (2, 3), (4, 3)])
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_tiled_head_is_bit_identical_to_row_major(wtype, B, k, T):
+    V, d, nd = 3001, 512, 1111
+    rng = np.random.default_rng(B * 100 + k)
+    head = synth.make_head(rng, V, d, wtype)
+    h_v, h_d = synth.make_hidden(rng, B, k, d)
+    hv, hd = dev_hidden(synth.encode_hidden(h_v, "bf16")), dev_hidden(synth.encode_hidden(h_d, "bf16"))
+    outs = []
+    for tiled in (False, True):
+        gc = GpuCycle(dev_head(head, tiled=tiled), nd, B, k, T, seed=3, eos=2)
+        g = gc.run(hd, hv, cycle=4)
+        g["raw_vstats"] = gc.row_stats.cpu().numpy()
+        g["raw_dstats"] = gc.draft_stats.cpu().numpy()
+        outs.append(g)
+    a, b = outs
+    for key in ("drafts", "tokens", "n_accept", "n_emit", "flags", "raw_vstats", "raw_dstats"):
+        assert np.array_equal(a[key], b[key]), key
+    if T > 0:
+        assert np.array_equal(a["logits"].view(np.uint32), b["logits"].view(np.uint32))
+        assert np.array_equal(a["draft_logits"].view(np.uint32), b["draft_logits"].view(np.uint32))
+
+
+@pytest.mark.parametrize("wtype", ["bf16", "q4a32"])
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_tiled_planted_depths_against_oracle(wtype, T):
+    V, d, nd, k, B = 4096, 256, 1024, 7, 2
+    rng = np.random.default_rng(15)
+    head = synth.make_head(rng, V, d, wtype, keep_source=True)
+    W = O.head_weights_f64(head)
+    gc = GpuCycle(dev_head(head, tiled=True), nd, B, k, T, seed=1234, eos=2)
+    for cyc in range(4):
+        h_v, h_d = synth.make_hidden(rng, B, k, d)
+        depths = [(2 * cyc + b * 3) % (k + 1) for b in range(B)]
+        targets = rng.integers(3, nd, size=(B, k + 1))
+        synth.plant_rows(head, h_v, h_d, depths, targets, (targets + 9) % nd, margin=12.0)
+        hv, hd = synth.encode_hidden(h_v, "bf16"), synth.encode_hidden(h_d, "bf16")
+        o = O.cycle(W, nd, O.hidden_f64(hd, "bf16"), O.hidden_f64(hv, "bf16"), T, 1234, cyc, 2, 2e-2)
+        g = gc.run(dev_hidden(hd), dev_hidden(hv), cycle=cyc)
+        check_cycle(g, o, T, 2e-2, tag=f"tiled {wtype} T{T} cycle {cyc}")
