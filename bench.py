@@ -27,7 +27,9 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 METRIC = "verify cycles/s (k=7, V=152,064, d=2560 bf16) + achieved HBM GB/s vs peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_head_amd", "csrc", "lmhead.hip")
+# sources the LM-head kernels are compiled from: counters taken on other sources are stale
+KERNEL_SRCS = [os.path.join(ROOT, "speculative_decoding_head_amd", "csrc", f)
+               for f in ("lmhead.hip", "lmhead_wide.hip", "lmhead_common.hpp", "common.hpp", "kernels.hpp")]
 
 # recurrent state and KV per request (the model's 36 recurrent layers x 16 heads x 128x128
 # fp32, 12 attention layers with fp16 4 x 256 KV rows)
@@ -74,9 +76,11 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> None:
     fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
 
     def copy_kernel(per):
-        cands = [k for k in per if "copyBuffer" in k or "direct_copy" in k or "elementwise" in k and "copy" in k]
-        best = max(cands, key=lambda k: max(per[k]))
-        return max(per[best])
+        # the calibration copy is the multiply-by-one elementwise kernel over COPY_BYTES
+        cands = [k for k in per if "elementwise" in k and "Mul" in k]
+        if not cands:
+            raise SystemExit("no calibration copy kernel in the counter CSV (run bench.py --calibrate-copy)")
+        return max(max(per[k]) for k in cands)
 
     f_scale = COPY_BYTES / copy_kernel(fetch)
     w_scale = COPY_BYTES / copy_kernel(write)
@@ -100,7 +104,11 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> None:
 
 
 def source_digest() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        if os.path.exists(f):
+            h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel: str, units_per_launch: float):
@@ -203,10 +211,12 @@ def main():
                 events[k + 3].record(stream)
 
     if args.calibrate_copy:
+        # a plain kernel copy of known size (multiply by one: reads and writes COPY_BYTES);
+        # copy_ itself would go to the DMA engine and show no kernel counters
         a = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
         a.fill_(1)
-        b.copy_(a)
+        torch.mul(a, 1, out=b)
         torch.cuda.synchronize()
         del a, b
 
