@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="model_greedy", choices=["model_greedy", "q4_greedy", "q4_sampled"])
+    ap.add_argument("--workload", default="model_greedy", choices=["model_greedy", "q4_greedy", "q4_sampled", "batched_commit"])
     ap.add_argument("--cpu-cycles", type=int, default=0, help="oracle cycles for the CPU baseline (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-commit", action="store_true", help="leave the commit out of the step")
@@ -260,7 +260,8 @@ def main():
                 "algorithmic_bytes_per_launch": int(bytes_per_launch)}
 
     draft_kernel = "mtp_draft_head_kernel"
-    verify_kernel = "mtp_verify_logits_kernel"
+    # up to 16 rows one kernel; 17..128 rows the wide kernel plus its per-row merge
+    verify_kernel = "mtp_verify_logits_kernel" if B * (k + 1) <= 16 else "mtp_verify_wide_kernel"
     dominant = "draft" if k * d_avg >= v_avg else "verify"
     roofline = roof(draft_bytes, d_avg, draft_kernel) if dominant == "draft" else roof(verify_bytes, v_avg, verify_kernel)
 

@@ -180,7 +180,7 @@ size_t mtp_workspace_bytes(int32_t op, int32_t rows, int32_t n_vocab_rows, int32
  * draft_stats:   mtp_row_stats [B][k_max]; writes column `slot`.
  * draft_logits:  float [B][k_max][n_draft] raw (unsanitised) logits, writes slot `slot`;
  *                required when T > 0 (the residual needs q), may be NULL at T = 0.
- * 1 <= n_draft <= vocab; 1 <= B <= 128; 0 <= slot < k_max <= 7.                       */
+ * 1 <= n_draft <= vocab; 1 <= B <= 16; 0 <= slot < k_max <= 7.                        */
 int mtp_draft_head(const mtp_head* head, int32_t n_draft, const void* hidden, int32_t htype,
                    int32_t B, int32_t slot, int32_t k_max, const mtp_sampling* smp,
                    int32_t* draft_tokens, mtp_row_stats* draft_stats, float* draft_logits,

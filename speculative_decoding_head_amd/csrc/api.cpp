@@ -74,7 +74,8 @@ size_t mtp_workspace_bytes(int32_t op, int32_t rows, int32_t n_vocab_rows, int32
   switch (op) {
     case MTP_OP_DRAFT:
     case MTP_OP_VERIFY:
-      if (rows < 1 || rows > kLmheadMaxRows || n_vocab_rows < 1) return 0;
+      if (rows < 1 || n_vocab_rows < 1) return 0;
+      if (rows > (op == MTP_OP_VERIFY ? kLmheadMaxWideRows : kLmheadMaxRows)) return 0;
       return lmhead_ws_bytes(rows, n_vocab_rows);
     case MTP_OP_ACCEPT:
       if (B < 1 || n_vocab_rows < 1) return 0;
@@ -172,11 +173,12 @@ int mtp_verify_logits(const mtp_head* head, const void* hidden, int32_t htype, i
   if (k < 1 || k > kMaxK || k_max < k || k_max > kMaxK) return MTP_ERR_SHAPE;
   if (B < 1) return MTP_ERR_SHAPE;
   const int M = B * (k + 1);
-  if (M > kLmheadMaxRows) return MTP_ERR_SHAPE;
+  if (M > kLmheadMaxWideRows) return MTP_ERR_SHAPE;
+  const bool wide = M > kLmheadMaxRows;
   const bool sampled = smp->temperature > 0.0f;
   if (sampled && !logits) return MTP_ERR_NULL;
   if (!aligned16(hidden) || !aligned16(row_stats) || (logits && !aligned16(logits))) return MTP_ERR_ALIGN;
-  if (lmhead_lds_bytes_for(head->wtype, head->d, M) > kMaxLds) return MTP_ERR_SHAPE;
+  if ((wide ? lmhead_wide_lds_bytes() : lmhead_lds_bytes_for(head->wtype, head->d, M)) > kMaxLds) return MTP_ERR_SHAPE;
   if (!ws || !aligned256(ws)) return ws ? MTP_ERR_ALIGN : MTP_ERR_WORKSPACE;
   if (ws_bytes < lmhead_ws_bytes(M, head->vocab)) return MTP_ERR_WORKSPACE;
 
@@ -210,7 +212,9 @@ int mtp_verify_logits(const mtp_head* head, const void* hidden, int32_t htype, i
   p.logits = logits;
   p.logits_stride = head->vocab;
   p.ws = ws;
-  return launch_lmhead(p, static_cast<hipStream_t>(stream)) == hipSuccess ? MTP_OK : MTP_ERR_HIP;
+  const hipError_t e = wide ? launch_lmhead_wide(p, static_cast<hipStream_t>(stream))
+                            : launch_lmhead(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MTP_OK : MTP_ERR_HIP;
 }
 
 int mtp_accept_sample(int32_t B, int32_t k, int32_t k_max, int32_t vocab, int32_t n_draft,

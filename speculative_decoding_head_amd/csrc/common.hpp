@@ -103,11 +103,22 @@ __device__ __forceinline__ void rowacc_init(RowAcc& a) {
   a.nonfinite = 0; a.nposinf = 0; a.pinf_min = kNoIndex; a.pg = kNegInf; a.pgidx = kNoIndex;
 }
 
+// z / T_eff and z / T_eff + G, each rounded on its own (never fused into one multiply-add),
+// so that every kernel scoring a logit produces the same bits
+__device__ __forceinline__ float score_scaled(float z, float inv_t) {
+#pragma clang fp contract(off)
+  return z * inv_t;
+}
+__device__ __forceinline__ float score_gumbel(float sv, float gumbel) {
+#pragma clang fp contract(off)
+  return sv + gumbel;
+}
+
 template <bool SAMPLED>
 __device__ __forceinline__ void rowacc_push(RowAcc& a, float z, int x, float inv_t, float gumbel) {
   if (__builtin_isfinite(z)) {
     if (z > a.zmax) { a.zmax = z; a.imax = x; }
-    const float sv = z * inv_t;
+    const float sv = score_scaled(z, inv_t);
     if (sv > a.m) {
       a.s = a.s * __expf(a.m - sv) + 1.0f;
       a.m = sv;
@@ -115,7 +126,7 @@ __device__ __forceinline__ void rowacc_push(RowAcc& a, float z, int x, float inv
       a.s += __expf(sv - a.m);
     }
     if (SAMPLED) {
-      const float sc = sv + gumbel;
+      const float sc = score_gumbel(sv, gumbel);
       if (sc > a.gbest) { a.gbest = sc; a.gidx = x; a.gz = z; }
     }
   } else {

@@ -16,6 +16,7 @@ namespace mtp {
 int lmhead_grid(int n_rows);
 constexpr int kLmheadThreads = 512;
 constexpr int kLmheadMaxRows = 16;        // hidden rows per launch of the LM-head kernels
+constexpr int kLmheadMaxWideRows = 128;   // hidden rows per launch of the wide verify kernel
 constexpr size_t kPartialBytes = 48;      // sizeof(RowAcc)
 constexpr int kAcceptThreads = 256;
 int accept_slices(int vocab, float temperature);
@@ -47,9 +48,16 @@ struct LmheadLaunch {
   void* ws;               // partials, drafted-logit slots, completion counter
 };
 
+// LM-head workspace: completion counter at 0, drafted-id logits at 256 (one float per
+// hidden row), then the [grid][M] block partials
+__host__ __device__ inline size_t lmhead_partials_offset(int M) { return 256 + ((size_t)(M * 4 + 255) / 256) * 256; }
 size_t lmhead_ws_bytes(int M, int n_rows);
 size_t lmhead_lds_bytes_for(int wtype, int d, int M);   // LDS a launch needs
 hipError_t launch_lmhead(const LmheadLaunch& p, hipStream_t stream);
+// verify pass for kLmheadMaxRows < M <= kLmheadMaxWideRows: the wide kernel, then one
+// merge block per hidden row
+size_t lmhead_wide_lds_bytes();
+hipError_t launch_lmhead_wide(const LmheadLaunch& p, hipStream_t stream);
 
 struct AcceptLaunch {
   int B, k, k_max, vocab, n_draft;

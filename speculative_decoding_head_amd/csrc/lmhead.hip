@@ -209,15 +209,10 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
     frag[f] = v;
   }
   if (L::q4) {
-    // per 32-value group and hidden row: sum of the hidden values, in k order
+    // per 32-value group and hidden row: sum of the hidden values
     for (int e = tid; e < nsteps * 16; e += kLmheadThreads) {
       const int s = e >> 4, i = e & 15;
-      float acc = 0.0f;
-      if (i < M) {
-        const uint16_t* h = static_cast<const uint16_t*>(p.hidden) + (size_t)i * d + 32 * s;
-        for (int kk = 0; kk < 32; ++kk) acc += bf16_to_f32(h[kk]);
-      }
-      htab[e] = acc;
+      htab[e] = i < M ? group_sum32(static_cast<const uint16_t*>(p.hidden) + (size_t)i * d + 32 * s) : 0.0f;
     }
   }
   __syncthreads();
@@ -301,7 +296,7 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   unsigned char* ws = static_cast<unsigned char*>(p.ws);
   unsigned int* counter = reinterpret_cast<unsigned int*>(ws);
   float* ztok = reinterpret_cast<float*>(ws + 256);
-  const size_t part_off = 256 + ((size_t)(M * 4 + 255) / 256) * 256;
+  const size_t part_off = lmhead_partials_offset(M);
   const int G = gridDim.x;
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(ws + part_off, (uint32_t)((size_t)G * M * sizeof(RowAcc)));
   if (tid < M) {
@@ -372,7 +367,7 @@ int lmhead_grid(int n_rows) {
 }
 
 size_t lmhead_ws_bytes(int M, int n_rows) {
-  return 256 + ((size_t)(M * 4 + 255) / 256) * 256 + (size_t)lmhead_grid(n_rows) * M * kPartialBytes;
+  return lmhead_partials_offset(M) + (size_t)lmhead_grid(n_rows) * M * kPartialBytes;
 }
 
 static size_t lmhead_lds_bytes(int wtype, int d, int M) {

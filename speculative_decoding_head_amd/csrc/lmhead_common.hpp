@@ -22,6 +22,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
 __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
@@ -50,6 +53,27 @@ __device__ __forceinline__ uint4 q4_expand(uint32_t w) {
 __device__ __forceinline__ uint4 q4_order(uint4 v) {
   return uint4{(v.x & 0xFFFFu) | (v.y << 16), (v.x >> 16) | (v.y & 0xFFFF0000u),
                (v.z & 0xFFFFu) | (v.w << 16), (v.z >> 16) | (v.w & 0xFFFF0000u)};
+}
+
+// Sum of one 32-value group of bf16 hidden values (64 contiguous, 16-byte aligned bytes) in
+// one fixed order that every kernel uses: each quarter of 8 values left to right, then
+// (q0 + q1) + (q2 + q3).
+__device__ __forceinline__ float group_sum32(const uint16_t* h) {
+  float q[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint4 v = *reinterpret_cast<const uint4*>(h + 8 * c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float a = __uint_as_float(w[0] << 16);
+    a += __uint_as_float(w[0] & 0xFFFF0000u);
+#pragma unroll
+    for (int e = 1; e < 4; ++e) {
+      a += __uint_as_float(w[e] << 16);
+      a += __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+    q[c] = a;
+  }
+  return (q[0] + q[1]) + (q[2] + q[3]);
 }
 
 template <int WT>

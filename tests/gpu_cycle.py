@@ -61,7 +61,7 @@ class GpuCycle:
         self.n_emit = torch.zeros(B, dtype=torch.int32, device=dev)
         self.flags = torch.zeros(B, dtype=torch.int32, device=dev)
         nb = max(mtp.workspace_bytes(mtp.OP_DRAFT, min(B, 16), n_draft, B),
-                 mtp.workspace_bytes(mtp.OP_VERIFY, min(B * (k + 1), 16), V, B),
+                 mtp.workspace_bytes(mtp.OP_VERIFY, min(B * (k + 1), 128), V, B),
                  mtp.workspace_bytes(mtp.OP_ACCEPT, 0, V, B))
         self.ws = mtp.workspace(nb)
 

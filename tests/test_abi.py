@@ -54,7 +54,10 @@ def test_workspace_bytes(lib):
     draft = mtp.workspace_bytes(mtp.OP_DRAFT, 1, 64000, 1)
     verify = mtp.workspace_bytes(mtp.OP_VERIFY, 8, 152064, 1)
     assert draft > 256 and verify > draft
-    assert mtp.workspace_bytes(mtp.OP_VERIFY, 17, 152064, 1) == 0      # more rows than one launch takes
+    # verify takes up to 128 rows (16 requests x 8), the draft head up to 16
+    assert mtp.workspace_bytes(mtp.OP_VERIFY, 128, 152064, 16) > mtp.workspace_bytes(mtp.OP_VERIFY, 17, 152064, 16) > verify
+    assert mtp.workspace_bytes(mtp.OP_VERIFY, 129, 152064, 1) == 0      # more rows than one launch takes
+    assert mtp.workspace_bytes(mtp.OP_DRAFT, 17, 64000, 17) == 0
     assert mtp.workspace_bytes(mtp.OP_DRAFT, 0, 10, 1) == 0
     assert mtp.workspace_bytes(99, 1, 10, 1) == 0
     assert mtp.workspace_bytes(mtp.OP_ACCEPT, 0, 152064, 16) > 0
@@ -114,7 +117,8 @@ def test_draft_head_rejects_bad_arguments(lib, case, want):
 
 @pytest.mark.parametrize("case,want", [
     (dict(k=0), -2), (dict(k=8, k_max=8), -2), (dict(k=4, k_max=3), -2),
-    (dict(B=3, k=7, k_max=7), -2),                               # 24 rows > 16 per launch
+    (dict(B=17, k=7, k_max=7), -2),                              # 136 rows > 128 per launch
+    (dict(B=16, k=7, k_max=7, ws_bytes=4096), -6),               # 128 rows: workspace too small
     (dict(drafts=None), -1), (dict(stats=None), -1),
     (dict(ws_bytes=1000), -6),
 ])
