@@ -139,17 +139,23 @@ __device__ __forceinline__ void rowacc_push(RowAcc& a, float z, int x, float inv
   }
 }
 
+// (va, ia) ranks above (vb, ib): larger value, then lower id (bitwise, branch-free)
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+  return (va > vb) | ((va == vb) & (ia < ib));
+}
+
+// Sum-exp of two parts with maxima ma, mb: the larger part's sum stays as it is and the
+// other is scaled by exp(-|ma - mb|) (one exponential).  Commutative bit for bit.
+__device__ __forceinline__ float sumexp_merge(float ma, float sa, float mb, float sb) {
+  const bool ge = ma >= mb;
+  const float e = (ma == kNegInf || mb == kNegInf) ? 0.0f : __expf(ge ? mb - ma : ma - mb);
+  return ge ? sa + sb * e : sb + sa * e;
 }
 
 // a <- merge(a, b).  Commutative: merge(a, b) and merge(b, a) give the same bits.
 __device__ __forceinline__ void rowacc_merge(RowAcc& a, const RowAcc& b) {
-  const float m = fmaxf(a.m, b.m);
-  const float sa = (a.m == kNegInf) ? 0.0f : a.s * __expf(a.m - m);
-  const float sb = (b.m == kNegInf) ? 0.0f : b.s * __expf(b.m - m);
-  a.m = m;
-  a.s = sa + sb;
+  a.s = sumexp_merge(a.m, a.s, b.m, b.s);
+  a.m = fmaxf(a.m, b.m);
   if (better(b.zmax, b.imax, a.zmax, a.imax)) { a.zmax = b.zmax; a.imax = b.imax; }
   if (better(b.gbest, b.gidx, a.gbest, a.gidx)) { a.gbest = b.gbest; a.gidx = b.gidx; a.gz = b.gz; }
   a.nonfinite += b.nonfinite;
@@ -196,6 +202,44 @@ __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 // completion ticket: returns the number of blocks that arrived before this one
 __device__ __forceinline__ unsigned int take_ticket(unsigned int* counter) {
   return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Exchange between the lanes l and l ^ MASK (MASK = 1, 2, 4, 8, inside each row of 16
+// lanes) on the DPP network: VALU moves with no LDS round trip.  xor 1 and xor 2 are quad
+// permutations; xor 4 is the half-row mirror (l -> 7 - l in each 8) followed by the quad
+// reversal (l -> 3 - l in each 4); xor 8 is a rotation of the 16-lane row by 8.
+template <int MASK>
+__device__ __forceinline__ int xor16(int v) {
+  static_assert(MASK == 1 || MASK == 2 || MASK == 4 || MASK == 8, "lanes of one 16-lane row");
+  if constexpr (MASK == 1) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);    // quad [1,0,3,2]
+  if constexpr (MASK == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);    // quad [2,3,0,1]
+  if constexpr (MASK == 4) {
+    const int h = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);                  // row half-mirror
+    return __builtin_amdgcn_update_dpp(0, h, 0x1B, 0xF, 0xF, false);                          // quad [3,2,1,0]
+  }
+  return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);                           // row rotate by 8
+}
+template <int MASK>
+__device__ __forceinline__ float xor16(float v) {
+  return __int_as_float(xor16<MASK>(__float_as_int(v)));
+}
+
+template <int MASK>
+__device__ __forceinline__ RowAcc rowacc_xor16(const RowAcc& a) {
+  RowAcc b;
+  b.m = xor16<MASK>(a.m);
+  b.s = xor16<MASK>(a.s);
+  b.zmax = xor16<MASK>(a.zmax);
+  b.imax = xor16<MASK>(a.imax);
+  b.gbest = xor16<MASK>(a.gbest);
+  b.gidx = xor16<MASK>(a.gidx);
+  b.gz = xor16<MASK>(a.gz);
+  b.nonfinite = xor16<MASK>(a.nonfinite);
+  b.nposinf = xor16<MASK>(a.nposinf);
+  b.pinf_min = xor16<MASK>(a.pinf_min);
+  b.pg = xor16<MASK>(a.pg);
+  b.pgidx = xor16<MASK>(a.pgidx);
+  return b;
 }
 
 __device__ __forceinline__ RowAcc rowacc_shfl_xor(const RowAcc& a, int mask) {

@@ -280,11 +280,10 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   // ---- reduce: 16 lanes of a row group, then the block's waves -------------------
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-#pragma unroll
-    for (int mask = 1; mask < 16; mask <<= 1) {
-      const RowAcc o = rowacc_shfl_xor(acc[r], mask);
-      rowacc_merge(acc[r], o);
-    }
+    rowacc_merge(acc[r], rowacc_xor16<1>(acc[r]));
+    rowacc_merge(acc[r], rowacc_xor16<2>(acc[r]));
+    rowacc_merge(acc[r], rowacc_xor16<4>(acc[r]));
+    rowacc_merge(acc[r], rowacc_xor16<8>(acc[r]));
   }
   if (xi == 0) {
 #pragma unroll

@@ -27,8 +27,24 @@ namespace {
 using namespace lm;
 
 constexpr int kWaves = kLmheadThreads / 64;   // 8
-constexpr int WTV = 2;                        // tiles a wave works on at once
-constexpr int WU = 4;                         // K steps per staged chunk
+#ifndef MTP_WIDE_TV
+#define MTP_WIDE_TV 2
+#endif
+#ifndef MTP_WIDE_U
+#define MTP_WIDE_U 4
+#endif
+#ifndef MTP_WIDE_SKIP_IDLE
+#define MTP_WIDE_SKIP_IDLE 0
+#endif
+#ifndef MTP_WIDE_GRID
+#define MTP_WIDE_GRID 0
+#endif
+constexpr int WTV = MTP_WIDE_TV;              // tiles a wave works on at once
+constexpr int WU = MTP_WIDE_U;                // K steps per staged chunk
+#ifndef MTP_WIDE_NB
+#define MTP_WIDE_NB 2
+#endif
+constexpr int NB = MTP_WIDE_NB;               // weight chunks in registers (NB-1 in flight)
 constexpr int NCB = 8;                        // column blocks of 16 hidden rows
 constexpr int kRows = NCB * 16;               // 128
 constexpr int kFragsPerChunk = WU * NCB * 64; // 16-byte A fragments per chunk
@@ -47,6 +63,15 @@ constexpr int kOffRun = kOffReq + kRows * 4;
 constexpr int kOffGum = kOffRun + kWaves * kRows * (int)sizeof(RowAcc);
 constexpr int kLdsBytes = kOffGum + kWaves * 4 * 16 * 16 * 4;
 
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled by construction
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 // running max / sum-exp / argmax and Gumbel best of a set of finite logits of one row (the
 // verify pass reports the sampled id, not its logit)
 struct Tuple {
@@ -59,11 +84,7 @@ struct Tuple {
 
 // commutative: merge(a, b) and merge(b, a) give the same bits
 __device__ __forceinline__ void tuple_merge(Tuple& a, const Tuple& b, float inv_t) {
-  const float ma = score_scaled(a.zmax, inv_t), mb = score_scaled(b.zmax, inv_t);
-  const float m = fmaxf(ma, mb);
-  const float sa = (a.zmax == kNegInf) ? 0.0f : a.s * __expf(ma - m);
-  const float sb = (b.zmax == kNegInf) ? 0.0f : b.s * __expf(mb - m);
-  a.s = sa + sb;
+  a.s = sumexp_merge(score_scaled(a.zmax, inv_t), a.s, score_scaled(b.zmax, inv_t), b.s);
   if (better(b.zmax, b.imax, a.zmax, a.imax)) { a.zmax = b.zmax; a.imax = b.imax; }
   if (better(b.gbest, b.gidx, a.gbest, a.gidx)) { a.gbest = b.gbest; a.gidx = b.gidx; }
 }
@@ -75,6 +96,17 @@ __device__ __forceinline__ Tuple tuple_shfl_xor(const Tuple& a, int mask) {
   b.s = __shfl_xor(a.s, mask);
   b.gbest = __shfl_xor(a.gbest, mask);
   b.gidx = __shfl_xor(a.gidx, mask);
+  return b;
+}
+
+template <int MASK>
+__device__ __forceinline__ Tuple tuple_xor16(const Tuple& a) {
+  Tuple b;
+  b.zmax = xor16<MASK>(a.zmax);
+  b.imax = xor16<MASK>(a.imax);
+  b.s = xor16<MASK>(a.s);
+  b.gbest = xor16<MASK>(a.gbest);
+  b.gidx = xor16<MASK>(a.gidx);
   return b;
 }
 
@@ -100,7 +132,7 @@ __device__ __forceinline__ void wide_body(const LmheadLaunch& p) {
   const int xi = lane & 15, g = lane >> 4;
   const int M = p.M, d = p.d;
   const int nsteps = L::f32 ? d / 16 : d / 32;
-  const int nch = ((nsteps + WU - 1) / WU + 1) & ~1;   // chunks per pass, even
+  const int nch = ((nsteps + WU - 1) / WU + NB - 1) / NB * NB;   // chunks per pass, a multiple of NB
 
   float* htab = reinterpret_cast<float*>(smem + kOffHtab);       // [2][WU][128] group sums of h
   uint4* hbuf = reinterpret_cast<uint4*>(smem + kOffHbuf);      // [2][WU][NCB][4][16] A fragments
@@ -237,27 +269,27 @@ __device__ __forceinline__ void wide_body(const LmheadLaunch& p) {
   };
   // chunk ch of the current pass, hidden fragments from LDS buffer buf.  Steps past the
   // end (padding of the last chunk) multiply zero weights by zero hidden values.
-  auto comp = [&](const Chunk& ck, int ch, int buf) {
+  auto comp = [&](const Chunk& ck, int ch, int buf, auto u0_c, auto u1_c) {
 #pragma unroll
-    for (int u = 0; u < WU; ++u) {
+    for (int u = decltype(u0_c)::value; u < decltype(u1_c)::value; ++u) {
       const int s = ch * WU + u;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         const uint4 a = hbuf[buf * kFragsPerChunk + ((u * NCB + cb) * 4 + g) * 16 + xi];
         if constexpr (WT == MTP_W_BF16 || WT == MTP_W_BF16_TILED) {
 #pragma unroll
-          for (int t = 0; t < WTV; ++t)
-            c[t][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(ck.w[t][u]), c[t][cb], 0, 0, 0);
+          for (int t = 0; t < WTV; ++t)   // weights as A: D[vocab row][hidden row]
+            c[t][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ck.w[t][u]), as_bf16x8(a), c[t][cb], 0, 0, 0);
         } else if constexpr (L::f32) {
           const float a0 = __uint_as_float(a.x), a1 = __uint_as_float(a.y);
           const float a2 = __uint_as_float(a.z), a3 = __uint_as_float(a.w);
 #pragma unroll
           for (int t = 0; t < WTV; ++t) {
             const uint4 w = ck.w[t][u];
-            c[t][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, __uint_as_float(w.x), c[t][cb], 0, 0, 0);
-            c[t][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, __uint_as_float(w.y), c[t][cb], 0, 0, 0);
-            c[t][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, __uint_as_float(w.z), c[t][cb], 0, 0, 0);
-            c[t][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a3, __uint_as_float(w.w), c[t][cb], 0, 0, 0);
+            c[t][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.x), a0, c[t][cb], 0, 0, 0);
+            c[t][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.y), a1, c[t][cb], 0, 0, 0);
+            c[t][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.z), a2, c[t][cb], 0, 0, 0);
+            c[t][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.w), a3, c[t][cb], 0, 0, 0);
           }
         } else {
           // 4-bit affine: D = sum (128 + q) h over the group, then z += s D + (min - 128 s) sum(h)
@@ -288,22 +320,249 @@ __device__ __forceinline__ void wide_body(const LmheadLaunch& p) {
     }
   };
 
-  // ---- per-tile epilogue --------------------------------------------------------------
-  // Lane (xi, g) holds, for column block cb, the logits of hidden rows cb*16 + 4g + r at
-  // vocabulary row x = 16 tile + xi.  Half h of the column blocks (cb = 4h .. 4h+3) gives
-  // 16 rows per lane, indexed n = 4 (cb - 4h) + r.  A transposed butterfly over the 16
-  // lanes of the row group halves the rows a lane carries at every level (lanes with bit m
-  // of xi set keep the upper half), so that lane xi ends up with row n = xi of the tile.
-  // Its running state lives in LDS (one slot per wave and row) between tiles.
-  float* ztok = reinterpret_cast<float*>(static_cast<unsigned char*>(p.ws) + 256);
-  auto epilogue = [&](int pass) {
+  // ---- epilogue of a pass, bf16 and fp32 heads ------------------------------------------
+  // With the weights as the MFMA A operand, lane (i, q) holds for tile t and column block
+  // cb the logits of hidden row j = cb*16 + i at the four consecutive vocabulary rows
+  // x = 16 tile + 4q + r.  Each lane keeps, for its 8 hidden rows, a running max, argmax,
+  // sum-exp (and Gumbel best) over its own vocabulary rows: no lane exchange until the end
+  // of the kernel.  A pass that holds a NaN or an infinity goes through full row statistics
+  // instead, merged into this wave's LDS slot for the row.
+  float* ztok = reinterpret_cast<float*>(static_cast<unsigned char*>(p.ws) + 256);   // drafted-id logits
+  float fz[NCB], fm[NCB], fs[NCB], fg[NCB];
+  int fi[NCB], fgi[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    fz[cb] = kNegInf; fm[cb] = kNegInf; fs[cb] = 0.0f; fg[cb] = kNegInf;
+    fi[cb] = kNoIndex; fgi[cb] = kNoIndex;
+  }
+  auto epilogue_t = [&](int pass) {
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));   // keeps per-row addresses out of the compute loop
+    const int li = lane_o & 15, q = lane_o >> 4;
+    const int tb = t_begin + pass * WTV;
+    if (tb >= t_end) return;   // wave-uniform
+    bool tval[WTV];
+    int x4[WTV];
+#pragma unroll
+    for (int t = 0; t < WTV; ++t) {
+      tval[t] = tb + t < t_end;
+      x4[t] = (tb + t) * 16 + 4 * q;
+    }
+    // bitwise, not short-circuit: 64 branches otherwise
+    uint32_t bad = 0;
+#pragma unroll
+    for (int t = 0; t < WTV; ++t)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          bad |= (uint32_t)(tval[t] & (x4[t] + r < p.n_rows)) & (uint32_t)!__builtin_isfinite(c[t][cb][r]);
+    const bool all_fin = __all(bad == 0);
+
+    if (p.logits) {   // raw logits: four consecutive ids per lane and row
+      const bool vec = (p.logits_stride & 3) == 0;   // rows 16-byte aligned (wave-uniform)
+#pragma unroll
+      for (int t = 0; t < WTV; ++t) {
+        if (!tval[t]) continue;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const int j = cb * 16 + li;
+          if (j >= M) continue;
+          float* dst = p.logits + (long long)j * p.logits_stride + x4[t];
+          if (vec && x4[t] + 3 < p.n_rows) {
+            *reinterpret_cast<f32x4*>(dst) = c[t][cb];
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (x4[t] + r < p.n_rows) dst[r] = c[t][cb][r];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < WTV; ++t) {   // the drafted-id logits
+      if (!tval[t]) continue;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int j = cb * 16 + li, tok = ltok[j];
+        if ((tok >= 0) & ((tok & ~3) == x4[t]) & (j < M)) {
+          const int r = tok & 3;
+          ztok[j] = r == 0 ? c[t][cb][0] : (r == 1 ? c[t][cb][1] : (r == 2 ? c[t][cb][2] : c[t][cb][3]));
+        }
+      }
+    }
+
+    if (all_fin) {
+      constexpr float kLog2e = 1.4426950408889634f;
+      const float c1 = p.inv_t * kLog2e;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int j = cb * 16 + li;
+        const bool rowok = j < M;
+        // the pass's logits of row j at this lane; -inf where there is none
+        float zv[WTV * 4];
+        int xv[WTV * 4];
+#pragma unroll
+        for (int t = 0; t < WTV; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            xv[4 * t + r] = x4[t] + r;
+            zv[4 * t + r] = (rowok & tval[t] & (x4[t] + r < p.n_rows)) ? c[t][cb][r] : kNegInf;
+          }
+        // max and its lowest id (ids increase with k)
+        float zm = zv[0];
+        int im = (zv[0] > kNegInf) ? xv[0] : kNoIndex;
+#pragma unroll
+        for (int k = 1; k < WTV * 4; ++k) {
+          const bool up = zv[k] > zm;
+          zm = up ? zv[k] : zm;
+          im = up ? xv[k] : im;
+        }
+        if (zm > kNegInf) {
+          const bool up = zm > fz[cb];   // a tie keeps the earlier (lower) id
+          const float zn = up ? zm : fz[cb];
+          fi[cb] = up ? im : fi[cb];
+          fz[cb] = zn;
+          // sum of exp(z/T - max/T): the old sum rescaled, the new terms added
+          const float mn = score_scaled(zn, p.inv_t);
+          const float c0 = -mn * kLog2e;
+          float acc = fs[cb] * __builtin_amdgcn_exp2f((fm[cb] - mn) * kLog2e);   // 0 while fm = -inf
+          if (fm[cb] == kNegInf) acc = 0.0f;
+#pragma unroll
+          for (int k = 0; k < WTV * 4; ++k) acc += __builtin_amdgcn_exp2f(fmaf(zv[k], c1, c0));
+          fs[cb] = acc;
+          fm[cb] = mn;
+        }
+        if (SAMPLED) {
+#pragma unroll
+          for (int t = 0; t < WTV; ++t) {
+            if (!tval[t]) continue;
+            // one Philox block = the Gumbel noise of these four ids
+            const u32x4 wd = philox4x32_10(u32x4{(uint32_t)x4[t] >> 2, lrow[j], lreq[j], p.cycle}, p.key0, p.key1);
+            const float gn[4] = {gumbel_from_word(wd.x), gumbel_from_word(wd.y), gumbel_from_word(wd.z),
+                                 gumbel_from_word(wd.w)};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float zr = zv[4 * t + r];
+              const float sc = score_gumbel(score_scaled(zr, p.inv_t), gn[r]);
+              const bool gup = (zr > kNegInf) & better(sc, xv[4 * t + r], fg[cb], fgi[cb]);
+              fg[cb] = gup ? sc : fg[cb];
+              fgi[cb] = gup ? xv[4 * t + r] : fgi[cb];
+            }
+          }
+        }
+      }
+    } else {
+      // a NaN or infinity in the pass (rare): full statistics per row, merged over the
+      // four lanes of the row, then into the wave's LDS slot
+      static_for<NCB>([&](auto cb_c) {   // compile-time column blocks: the accumulators stay in registers
+        constexpr int cb = decltype(cb_c)::value;
+        const int j = cb * 16 + li;
+        RowAcc a;
+        rowacc_init(a);
+#pragma unroll
+        for (int t = 0; t < WTV; ++t) {
+          if (!tval[t]) continue;
+          const f32x4 zz = c[t][cb];
+          u32x4 wd = u32x4{0u, 0u, 0u, 0u};
+          if (SAMPLED) wd = philox4x32_10(u32x4{(uint32_t)x4[t] >> 2, lrow[j], lreq[j], p.cycle}, p.key0, p.key1);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int x = x4[t] + r;
+            const float gnr = SAMPLED ? gumbel_from_word(r == 0 ? wd.x : (r == 1 ? wd.y : (r == 2 ? wd.z : wd.w))) : 0.0f;
+            if (j < M && x < p.n_rows) rowacc_push<SAMPLED>(a, zz[r], x, p.inv_t, gnr);
+          }
+        }
+        rowacc_merge(a, rowacc_shfl_xor(a, 16));
+        rowacc_merge(a, rowacc_shfl_xor(a, 32));
+        if (q == 0 && j < M) {
+          RowAcc run = lrun[wave * kRows + j];
+          rowacc_merge(run, a);
+          lrun[wave * kRows + j] = run;
+        }
+      });
+    }
+  };
+  // end of the kernel: each row's lane states merged over the four lanes that hold it,
+  // then with the wave's LDS slot (passes that went the slow way)
+  auto finish_t = [&]() {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      Tuple v{fz[cb], fi[cb], fs[cb], fg[cb], fgi[cb]};
+      tuple_merge(v, tuple_shfl_xor(v, 16), p.inv_t);
+      tuple_merge(v, tuple_shfl_xor(v, 32), p.inv_t);
+      const int j = cb * 16 + xi;
+      if (g == 0 && j < M) {
+        RowAcc run = lrun[wave * kRows + j];
+        rowacc_merge(run, tuple_to_rowacc(v, p.inv_t));
+        lrun[wave * kRows + j] = run;
+      }
+    }
+  };
+
+  // ---- epilogue of a pass, 4-bit heads --------------------------------------------------
+  // (The scales are per vocabulary row, so the weights stay the MFMA B operand.)
+  // Lane (xi, g) holds, for tile t of the pass and column block cb, the logits of hidden
+  // rows cb*16 + 4g + r at vocabulary row x_t = 16 (tile) + xi.  The lane first merges its
+  // WTV logits of each row (one exponential per extra tile).  Half h of the column blocks
+  // (cb = 4h .. 4h+3) then gives 16 rows per lane, indexed n = 4 (cb - 4h) + r; a
+  // transposed butterfly over the 16 lanes of the row group halves the rows a lane carries
+  // at every level (lanes with bit m of xi set keep the upper half), so that lane xi ends
+  // up with row n = xi.  Its running state lives in LDS (one slot per wave and row).
+  auto epilogue_q = [&](int pass) {
     // the lane coordinates again, opaque to the optimiser: otherwise per-row addresses and
     // indices of this code are hoisted out of the pass loop and held across the whole
     // compute loop
     int lane_o = lane;
     asm volatile("" : "+v"(lane_o));
     const int xi = lane_o & 15, g = lane_o >> 4;
-    // Gumbel noise of the 16 rows of half h at the tile's 16 vocabulary rows.  One Philox
+    const int tb = t_begin + pass * WTV;
+    bool tval[WTV], xin[WTV];
+    int xs[WTV];
+#pragma unroll
+    for (int t = 0; t < WTV; ++t) {
+      tval[t] = tb + t < t_end;   // wave-uniform
+      xs[t] = (tb + t) * 16 + xi;
+      xin[t] = tval[t] && xs[t] < p.n_rows;
+    }
+    if (!tval[0]) return;   // no tile in this pass (wave-uniform)
+
+    // raw logits (sampling needs them) and the drafted-id logits
+    if (p.logits) {
+#pragma unroll
+      for (int t = 0; t < WTV; ++t) {
+        float* lrow0 = p.logits + (long long)(4 * g) * p.logits_stride + xs[t];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (xin[t] && cb * 16 + 4 * g + r < M) lrow0[(long long)(cb * 16 + r) * p.logits_stride] = c[t][cb][r];
+      }
+    }
+    bool fin = true;
+#pragma unroll
+    for (int t = 0; t < WTV; ++t) {
+      uint32_t hit = 0;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int4 tk = *reinterpret_cast<const int4*>(ltok + cb * 16 + 4 * g);
+        hit |= (uint32_t)(xs[t] == tk.x) << (4 * cb) | (uint32_t)(xs[t] == tk.y) << (4 * cb + 1) |
+               (uint32_t)(xs[t] == tk.z) << (4 * cb + 2) | (uint32_t)(xs[t] == tk.w) << (4 * cb + 3);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) fin = fin & (!xin[t] | (bool)__builtin_isfinite(c[t][cb][r]));   // bitwise
+      }
+      if (!xin[t]) hit = 0;
+      if (hit) {   // rare: a drafted id inside this tile
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if ((hit >> (4 * cb + r)) & 1u) ztok[cb * 16 + 4 * g + r] = c[t][cb][r];
+      }
+    }
+    const bool all_fin = __all(fin);
+
+    // Gumbel noise of the 16 rows of half h at tile t's 16 vocabulary rows.  One Philox
     // block covers 4 consecutive ids of one row, so the 16 lanes of a row group compute the
     // 64 blocks of their rows once (lane 4m + a: rows n = 4a .. 4a+3, ids 16 tile + 4m ..
     // 4m+3) and hand the values over through this wave's LDS slice; lane xi then reads the
@@ -324,133 +583,142 @@ __device__ __forceinline__ void wide_body(const LmheadLaunch& p) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
     auto noise = [&](int n) -> float { return gum[(16 * g + n) * 16 + xi]; };
-    auto make_tuple = [&](float z, int n, int x, bool inc) -> Tuple {
-      Tuple v;
-      v.zmax = inc ? z : kNegInf;
-      v.imax = inc ? x : kNoIndex;
-      v.s = inc ? 1.0f : 0.0f;
-      v.gbest = kNegInf;
-      v.gidx = kNoIndex;
-      if (SAMPLED && inc) {
-        v.gbest = score_gumbel(score_scaled(z, p.inv_t), noise(n));
-        v.gidx = x;
-      }
-      return v;
-    };
-    const int tb = t_begin + pass * WTV;
+
 #pragma unroll
-    for (int t = 0; t < WTV; ++t) {
-      if (tb + t >= t_end) continue;   // wave-uniform
-      const int x = (tb + t) * 16 + xi;
-      const bool xin = x < p.n_rows;
-      bool fin = true;
+    for (int h = 0; h < 2; ++h) {
+      const int jo = (4 * h + xi / 4) * 16 + 4 * g + xi % 4;   // the row this lane ends up with
+      RowAcc pass_acc;
+      // sampled: best z/T + G over the pass's tiles for each of the half's 16 rows
+      float gsc[16];
+      int gix[16];
+      if (SAMPLED) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const int4 tk = *reinterpret_cast<const int4*>(ltok + cb * 16 + 4 * g);
+        for (int n = 0; n < 16; ++n) { gsc[n] = kNegInf; gix[n] = kNoIndex; }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = cb * 16 + 4 * g + r;
-          const float z = c[t][cb][r];
-          fin = fin && (!xin || __builtin_isfinite(z));
-          if (!xin || j >= M) continue;
-          if (p.logits) p.logits[(long long)j * p.logits_stride + x] = z;
-          const int tok = r == 0 ? tk.x : (r == 1 ? tk.y : (r == 2 ? tk.z : tk.w));
-          if (x == tok) ztok[j] = z;
+        for (int t = 0; t < WTV; ++t) {
+          if (!tval[t]) continue;   // wave-uniform
+          make_noise(tb + t, h);
+#pragma unroll
+          for (int n = 0; n < 16; ++n) {
+            const int cb = 4 * h + n / 4, r = n % 4;
+            const bool ok = xin[t] & (cb * 16 + 4 * g + r < M) & all_fin;
+            const float sc = ok ? score_gumbel(score_scaled(c[t][cb][r], p.inv_t), noise(n)) : kNegInf;
+            if (better(sc, ok ? xs[t] : kNoIndex, gsc[n], gix[n])) { gsc[n] = sc; gix[n] = xs[t]; }
+          }
         }
       }
-      const bool all_fin = __all(fin);
+      // the lane's merged tuple of row n (both tiles)
+      auto row_tuple = [&](int n, int cb, int r) -> Tuple {
+        Tuple v{kNegInf, kNoIndex, 0.0f, kNegInf, kNoIndex};
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int jo = (4 * h + xi / 4) * 16 + 4 * g + xi % 4;   // the row this lane ends up with
-        RowAcc tile_acc;
-        if (SAMPLED) make_noise(tb + t, h);
-        if (all_fin) {
-          // first level (mask 8) straight from the accumulators: rows n and n + 8 are column
-          // blocks 4h + n/4 and 4h + n/4 + 2
-          const bool hi8 = (xi & 8) != 0;
-          Tuple v[8];
+        for (int t = 0; t < WTV; ++t) {
+          const bool ok = xin[t] & (cb * 16 + 4 * g + r < M);
+          const Tuple e{ok ? c[t][cb][r] : kNegInf, ok ? xs[t] : kNoIndex, ok ? 1.0f : 0.0f, kNegInf, kNoIndex};
+          if (t == 0) v = e; else tuple_merge(v, e, p.inv_t);
+        }
+        if (SAMPLED) { v.gbest = gsc[n]; v.gidx = gix[n]; }
+        return v;
+      };
+      if (all_fin) {
+        // first level (mask 8) straight from the accumulators: rows n and n + 8 are column
+        // blocks 4h + n/4 and 4h + n/4 + 2
+        const bool hi8 = (xi & 8) != 0;
+        Tuple v[8];
 #pragma unroll
-          for (int n = 0; n < 8; ++n) {
-            const int cb = 4 * h + n / 4, r = n % 4;
-            const float zl = c[t][cb][r], zh = c[t][cb + 2][r];
-            const int jl = cb * 16 + 4 * g + r, jh = jl + 32;
-            const float zk = hi8 ? zh : zl, zs = hi8 ? zl : zh;
-            const int jk = hi8 ? jh : jl, js = hi8 ? jl : jh;
-            Tuple mine = make_tuple(zk, hi8 ? n + 8 : n, x, xin && jk < M);
-            const Tuple recv = tuple_shfl_xor(make_tuple(zs, hi8 ? n : n + 8, x, xin && js < M), 8);
+        for (int n = 0; n < 8; ++n) {
+          const int cb = 4 * h + n / 4, r = n % 4;
+          const Tuple lo = row_tuple(n, cb, r), hi = row_tuple(n + 8, cb + 2, r);
+          Tuple mine = hi8 ? hi : lo;
+          const Tuple recv = tuple_xor16<8>(hi8 ? lo : hi);
+          tuple_merge(mine, recv, p.inv_t);
+          v[n] = mine;
+        }
+        auto level = [&](auto mask_c) {
+          constexpr int mask = decltype(mask_c)::value, half = mask;
+          const bool hi = (xi & mask) != 0;
+#pragma unroll
+          for (int n = 0; n < half; ++n) {
+            Tuple mine = hi ? v[n + half] : v[n];
+            const Tuple send = hi ? v[n] : v[n + half];
+            const Tuple recv = tuple_xor16<mask>(send);
             tuple_merge(mine, recv, p.inv_t);
             v[n] = mine;
           }
-#pragma unroll
-          for (int lvl = 1; lvl < 4; ++lvl) {
-            const int mask = 8 >> lvl, half = 8 >> lvl;
-            const bool hi = (xi & mask) != 0;
-#pragma unroll
-            for (int n = 0; n < half; ++n) {
-              Tuple mine = hi ? v[n + half] : v[n];
-              const Tuple send = hi ? v[n] : v[n + half];
-              const Tuple recv = tuple_shfl_xor(send, mask);
-              tuple_merge(mine, recv, p.inv_t);
-              v[n] = mine;
-            }
-          }
-          tile_acc = tuple_to_rowacc(v[0], p.inv_t);
-        } else {
-          // a NaN or infinity in the tile (rare): full row statistics, one row at a time, with
-          // the same pairing of lanes as the butterfly above
-          rowacc_init(tile_acc);
+        };
+        level(std::integral_constant<int, 4>{});
+        level(std::integral_constant<int, 2>{});
+        level(std::integral_constant<int, 1>{});
+        pass_acc = tuple_to_rowacc(v[0], p.inv_t);
+      } else {
+        // a NaN or infinity in the pass (rare): full row statistics, one row at a time,
+        // with the same pairing of lanes as the butterfly above
+        rowacc_init(pass_acc);
 #pragma unroll 1
-          for (int n = 0; n < 16; ++n) {
+        for (int n = 0; n < 16; ++n) {
+          RowAcc a;
+          rowacc_init(a);
+          const int j = (4 * h + n / 4) * 16 + 4 * g + n % 4;
+#pragma unroll
+          for (int t = 0; t < WTV; ++t) {
+            if (!tval[t]) continue;   // wave-uniform
+            if (SAMPLED) make_noise(tb + t, h);
             float z = c[t][4 * h][0];
 #pragma unroll
             for (int q = 1; q < 16; ++q) z = (n == q) ? c[t][4 * h + q / 4][q % 4] : z;
-            const int j = (4 * h + n / 4) * 16 + 4 * g + n % 4;
-            RowAcc a;
-            rowacc_init(a);
-            if (xin && j < M) rowacc_push<SAMPLED>(a, z, x, p.inv_t, SAMPLED ? noise(n) : 0.0f);
-#pragma unroll
-            for (int mask = 8; mask >= 1; mask >>= 1) {
-              const RowAcc o = rowacc_shfl_xor(a, mask);
-              rowacc_merge(a, o);
-            }
-            if (xi == n) tile_acc = a;
+            if (xin[t] && j < M) rowacc_push<SAMPLED>(a, z, xs[t], p.inv_t, SAMPLED ? noise(n) : 0.0f);
           }
+          rowacc_merge(a, rowacc_xor16<8>(a));
+          rowacc_merge(a, rowacc_xor16<4>(a));
+          rowacc_merge(a, rowacc_xor16<2>(a));
+          rowacc_merge(a, rowacc_xor16<1>(a));
+          if (xi == n) pass_acc = a;
         }
-        RowAcc run = lrun[wave * kRows + jo];
-        rowacc_merge(run, tile_acc);
-        lrun[wave * kRows + jo] = run;
       }
+      RowAcc run = lrun[wave * kRows + jo];
+      rowacc_merge(run, pass_acc);
+      lrun[wave * kRows + jo] = run;
     }
   };
 
-  // ---- pipeline: while chunk it computes, hidden chunk it+1 and the weights of chunk
-  //      it+1 (the next pass's first chunk at the end of a pass) are in flight; hidden
-  //      loads are issued first so that waiting for them does not also wait for the
-  //      weights.  One barrier per chunk; the epilogue of a pass overlaps the next pass's
-  //      first loads. --------------------------------------------------------------------
-  Chunk A, B;
+  // ---- pipeline.  Chunk it's weights are issued NB-1 chunks ahead (NB register
+  //      buffers); its hidden fragments are loaded into registers at the end of chunk
+  //      it-2 and written to LDS (double buffer) at the end of chunk it-1.  Loads retire
+  //      in issue order, so the hidden loads are issued last in each chunk: waiting for
+  //      them never waits for weights issued after them.  One barrier per chunk; the
+  //      epilogue of a pass runs with the next pass's first chunks in flight.  A pass has
+  //      a multiple of NB chunks; chunks past the end of K only keep the pipeline in step.
+  Chunk Wb[NB];
   Staged S;
   stage_load(S, 0);
-  load(A, 0);
   stage_store(S, 0);
+#pragma unroll
+  for (int k = 0; k + 1 < NB; ++k) load(Wb[k], k);
+  stage_load(S, 1 % nch);
   __syncthreads();
   int it = 0;
+  bool busy = true;
+  auto step = [&](Chunk& cur, Chunk& ahead, int ch) {
+    load(ahead, it + NB - 1);
+    // the next chunk's hidden fragments go to LDS between the two halves of this chunk's
+    // MFMAs, so that the LDS writes overlap the second half
+    const bool act = busy && ch * WU < nsteps;
+    if (act) comp(cur, ch, it & 1, std::integral_constant<int, 0>{}, std::integral_constant<int, WU / 2>{});
+    stage_store(S, (it + 1) & 1);
+    if (act) comp(cur, ch, it & 1, std::integral_constant<int, WU / 2>{}, std::integral_constant<int, WU>{});
+    stage_load(S, (ch + 2) % nch);
+    __syncthreads();
+    ++it;
+  };
   for (int pass = 0; pass < npass; ++pass) {
     zero_acc();
-    for (int ch = 0; ch < nch; ch += 2, it += 2) {
-      stage_load(S, ch + 1);
-      load(B, it + 1);
-      comp(A, ch, 0);
-      stage_store(S, 1);
-      __syncthreads();
-      stage_load(S, ch + 2 < nch ? ch + 2 : 0);
-      load(A, it + 2);
-      comp(B, ch + 1, 1);
-      stage_store(S, 0);
-      __syncthreads();
+    busy = !MTP_WIDE_SKIP_IDLE || t_begin + pass * WTV < t_end;   // wave-uniform
+    for (int ch = 0; ch < nch; ch += NB) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) step(Wb[k], Wb[(k + NB - 1) % NB], ch + k);
     }
-    epilogue(pass);
+    if constexpr (L::q4) epilogue_q(pass); else epilogue_t(pass);
   }
+  if constexpr (!L::q4) finish_t();
 
   // ---- block partial per row: the waves' states merged in wave order, after every
   //      wave's last epilogue ----------------------------------------------------------
@@ -508,9 +776,30 @@ __global__ __launch_bounds__(kMergeThreads) void mtp_verify_wide_merge_kernel(Lm
 
 size_t lmhead_wide_lds_bytes() { return kLdsBytes; }
 
+// Blocks of the wide kernel for a head of n_rows vocabulary rows (a function of n_rows
+// only).  Every wave of a block runs the same number of passes, so the kernel takes about
+// passes x blocks pass-times of streaming; this picks the block count in
+// [lmhead_grid / 2, lmhead_grid] that minimises that product (fewest idle tile slots),
+// preferring more blocks on ties.  152,064 rows: 9,504 tiles = 198 blocks x 8 waves x 3
+// passes x 2 tiles exactly.
+static int wide_grid(int n_rows) {
+  const int tiles = (n_rows + 15) / 16;
+  const int gmax = lmhead_grid(n_rows);   // the workspace holds this many partials per row
+  int best = gmax;
+  long long best_cost = -1;
+  for (int G = gmax; G >= (gmax + 1) / 2; --G) {
+    const long long waves = (long long)G * kWaves;
+    const long long per_wave = (tiles + waves - 1) / waves;
+    const long long passes = (per_wave + WTV - 1) / WTV;
+    const long long cost = passes * G;
+    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = G; }
+  }
+  return best;
+}
+
 template <int WT, bool SAMPLED>
 static hipError_t launch_wide_t(const LmheadLaunch& p, hipStream_t stream) {
-  const int G = lmhead_grid(p.n_rows);
+  const int G = MTP_WIDE_GRID > 0 ? min(MTP_WIDE_GRID, lmhead_grid(p.n_rows)) : wide_grid(p.n_rows);
   const size_t lds = lmhead_wide_lds_bytes();
   auto kern = mtp_verify_wide_kernel<WT, SAMPLED>;
   if (lds > 65536) {
