@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0   # dense MFMA, bf16
 METRIC = "verify cycles/s (k=7, V=152,064, d=2560 bf16) + achieved HBM GB/s vs peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # sources the LM-head kernels are compiled from: counters taken on other sources are stale
@@ -47,6 +48,13 @@ def parse():
     ap.add_argument("--event-every", type=int, default=10,
                     help="record per-kernel HIP events in every N-th timed cycle (each event is a queue packet "
                          "that adds a few microseconds of gap, so timing every cycle would slow the cycles it times)")
+    ap.add_argument("--rotate-heads", type=int, default=3,
+                    help="after the timed region, time the draft head rotating over this many copies of the "
+                         "head (each call reads weights no cache holds); 0 or 1 = skip")
+    ap.add_argument("--planted-alpha", type=float, default=0.75,
+                    help="after the timed region, time whole cycles whose acceptance depth is planted per "
+                         "request with P(depth >= j) = alpha^j; 0 = skip")
+    ap.add_argument("--extra-cycles", type=int, default=30, help="cycles timed by each extra measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-commit", action="store_true", help="leave the commit out of the step")
     ap.add_argument("--row-major", action="store_true",
@@ -149,7 +157,8 @@ def main():
     # ---- inputs (seeded, synthetic), resident in HBM -----------------------------
     t0 = time.time()
     rng = np.random.default_rng(wl.seed)
-    head = synth.make_head(rng, wl.V, wl.d, wl.wtype)
+    # a 4-bit head keeps its fp32 draw on the host only to aim the planted rows
+    head = synth.make_head(rng, wl.V, wl.d, wl.wtype, keep_source=wl.wtype == "q4a32" and args.planted_alpha > 0)
     h_v, h_d = synth.make_hidden(rng, wl.B, wl.k, wl.d)
     hv = synth.encode_hidden(h_v, wl.htype)
     hd = synth.encode_hidden(h_d, wl.htype)
@@ -186,22 +195,23 @@ def main():
         snaps = torch.randint(0, 256, (B, k + 1, state_bytes), dtype=torch.uint8, device=dev, generator=g)
         live = torch.zeros(B, state_bytes, dtype=torch.uint8, device=dev)
         # room for every cycle's accepted rows, so the trim never saturates at the cache end
-        kv_rows = KV_ROWS + (k + 1) * (args.warmup + args.steps)
+        kv_rows = KV_ROWS + (k + 1) * (args.warmup + args.steps + 16 + args.extra_cycles)
         kv = torch.zeros(B, KV_LAYERS, 2, kv_rows, kv_row_bytes, dtype=torch.uint8, device=dev)
         kv_len = torch.zeros(B, dtype=torch.int32, device=dev)
     setup_s = time.time() - t0
 
     stream = torch.cuda.current_stream()
 
-    def cycle(c, events=None):
+    def cycle(c, events=None, hidden=None):
+        hv_c, hd_c = (hv_t, hd_slots) if hidden is None else hidden
         smp = mtp.sampling(T, wl.eos, wl.philox_seed, c, 0)
         if events is not None:
             events[0].record(stream)
         for i in range(k):
-            mtp.mtp_draft_head(dh, nd, hd_slots[i], i, k, smp, dtok, dst, dlg, ws, stream)
+            mtp.mtp_draft_head(dh, nd, hd_c[i], i, k, smp, dtok, dst, dlg, ws, stream)
             if events is not None:
                 events[1 + i].record(stream)
-        mtp.mtp_verify_logits(dh, hv_t, k, dtok, k, smp, vst, vlg, ws, stream)
+        mtp.mtp_verify_logits(dh, hv_c, k, dtok, k, smp, vst, vlg, ws, stream)
         if events is not None:
             events[k + 1].record(stream)
         mtp.mtp_accept_sample(B, k, k, V, nd, smp, dtok, dst, dlg, vst, vlg, out, nacc, nemit, flg, ws, stream)
@@ -257,13 +267,19 @@ def main():
     d_avg = float(np.mean(draft_ms)) * 1e-3
     v_avg = float(np.mean(verify_ms)) * 1e-3
 
-    def roof(bytes_per_launch, avg_s, kernel):
+    def roof(bytes_per_launch, avg_s, kernel, flops=None):
         ach = bytes_per_launch / avg_s / 1e9
         tr = load_traffic(kernel, 1)
-        return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": tr,
-                "kernel": kernel, "avg_launch_us": round(avg_s * 1e6, 2),
-                "algorithmic_bytes_per_launch": int(bytes_per_launch)}
+        r = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+             "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": tr,
+             "kernel": kernel, "avg_launch_us": round(avg_s * 1e6, 2),
+             "algorithmic_bytes_per_launch": int(bytes_per_launch)}
+        if flops is not None:
+            # the verify product runs on MFMA: its algorithmic rate against the dense bf16 peak
+            r["mfma"] = {"algorithmic_flops_per_launch": int(flops),
+                         "achieved_TFLOPs": round(flops / avg_s / 1e12, 1),
+                         "frac_of_dense_bf16_peak": round(flops / avg_s / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        return r
 
     draft_kernel = "mtp_draft_head_kernel"
     # up to 16 rows one kernel; 17..128 rows the wide kernel plus its per-row merge
@@ -290,7 +306,7 @@ def main():
                    "step": f"{k} draft-head calls + verify ({B * (k + 1)} rows) + accept"
                            + (" + commit (36 MiB snapshot select, 12-layer KV trim)" if with_commit else "")},
         "roofline": roofline,
-        "roofline_verify": roof(verify_bytes, v_avg, verify_kernel),
+        "roofline_verify": roof(verify_bytes, v_avg, verify_kernel, flops=2.0 * V * d * B * (k + 1)),
         "kernel_timing": f"HIP events around every launch in {len(timed)} of the {args.steps} timed cycles",
         "stages_us": {"draft_head_avg": round(d_avg * 1e6, 2), "verify_avg": round(v_avg * 1e6, 2),
                       "accept_avg": round(float(np.mean(accept_ms)) * 1e3, 2),
@@ -299,6 +315,74 @@ def main():
         "tokens_per_s": round(float(nemit.sum().item()) * value, 1),
         "setup_s": round(setup_s, 1),
     }
+
+    # ---- draft head against HBM proper: rotate over copies of the head, so that no
+    #      call finds the previous call's rows in the 256 MB last-level cache ------------
+    if args.rotate_heads > 1:
+        copies = [dh] + [mtp.Head(dh.wtype, dh.d, dh.vocab, dh.w.clone(),
+                                  None if dh.scale is None else dh.scale.clone(),
+                                  None if dh.minv is None else dh.minv.clone())
+                         for _ in range(args.rotate_heads - 1)]
+        smp = mtp.sampling(T, wl.eos, wl.philox_seed, 0, 0)
+        n = args.extra_cycles * k
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        for j in range(len(copies)):
+            mtp.mtp_draft_head(copies[j], nd, hd_slots[0], 0, k, smp, dtok, dst, dlg, ws, stream)
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for j in range(n):
+            mtp.mtp_draft_head(copies[j % len(copies)], nd, hd_slots[j % k], j % k, k, smp, dtok, dst, dlg, ws,
+                               stream)
+            ev[j + 1].record(stream)
+        torch.cuda.synchronize()
+        rot = float(np.mean([ev[j].elapsed_time(ev[j + 1]) for j in range(n)])) * 1e-3
+        result["draft_head_rotated"] = {"copies": len(copies), "launches": n, "avg_launch_us": round(rot * 1e6, 2),
+                                        "achieved_GBps": round(draft_bytes / rot / 1e9, 1),
+                                        "frac": round(draft_bytes / rot / 1e9 / PEAK_HBM_GBPS, 4)}
+        del copies
+        torch.cuda.empty_cache()
+
+    # ---- planted acceptance: whole cycles whose per-request depth is drawn with
+    #      P(depth >= j) = alpha^j (capped at k), planted into the hidden rows -----------
+    if args.planted_alpha > 0:
+        prng = np.random.default_rng(wl.seed + 7)
+        n_sets = 16
+        sets, depth_sum = [], 0
+        for _ in range(n_sets):
+            pv, pd = synth.make_hidden(prng, B, k, d)
+            depths = np.minimum(prng.geometric(1.0 - args.planted_alpha, size=B) - 1, k)
+            tg = prng.integers(0, nd, size=(B, k + 1))
+            alt = (tg + 1 + prng.integers(0, nd - 1, size=(B, k + 1))) % nd
+            synth.plant_rows(head, pv, pd, depths, tg, alt)
+            ev_, ed_ = synth.encode_hidden(pv, wl.htype), synth.encode_hidden(pd, wl.htype)
+            sets.append((torch.from_numpy(ev_.view(np.int16)).to(dev),
+                         [torch.from_numpy(np.ascontiguousarray(ed_[:, i]).view(np.int16)).to(dev) for i in range(k)]))
+            depth_sum += int(depths.sum())
+        emitted = torch.zeros(B, dtype=torch.int64, device=dev)
+        for c in range(n_sets):   # warm-up, also of the counter update (its first call loads a kernel)
+            cycle(c, hidden=sets[c])
+            emitted += nemit
+        emitted.zero_()
+        torch.cuda.synchronize()
+        pev = {c: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+               for c in range(args.extra_cycles) if c % every == 0}
+        t1 = time.perf_counter()
+        for c in range(args.extra_cycles):
+            cycle(c, pev.get(c), hidden=sets[c % n_sets])
+            emitted += nemit
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t1
+        tot = int(emitted.sum().item())
+        pst = {name: round(float(np.mean([e[a].elapsed_time(e[b]) for e in pev.values()])) * 1e3 / div, 2)
+               for name, a, b, div in (("draft_head_avg", 0, k, k), ("verify_avg", k, k + 1, 1),
+                                       ("accept_avg", k + 1, k + 2, 1))}
+        if with_commit:
+            pst["commit_avg"] = round(float(np.mean([e[k + 2].elapsed_time(e[k + 3]) for e in pev.values()])) * 1e3, 2)
+        result["planted_alpha"] = {
+            "alpha": args.planted_alpha, "cycles": args.extra_cycles, "hidden_sets": n_sets,
+            "cycles_per_s": round(args.extra_cycles / el, 2), "tokens_per_s": round(tot / el, 1),
+            "mean_tokens_per_request_cycle": round(tot / (args.extra_cycles * B), 3),
+            "planted_mean_depth": round(depth_sum / (n_sets * B), 3), "stages_us": pst}
 
     # ---- CPU baseline: the oracle, as it stands, on a bounded sample --------------
     if not args.no_cpu_baseline:

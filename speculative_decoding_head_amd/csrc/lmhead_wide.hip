@@ -184,41 +184,51 @@ __device__ __forceinline__ void wide_body(const LmheadLaunch& p) {
   auto load = [&](Chunk& ck, int it) {
     const int tb = t_begin + (it / nch) * WTV;
     const int s0 = (it % nch) * WU;
+    uint32_t roff[WTV];
 #pragma unroll
     for (int t = 0; t < WTV; ++t) {
       const int x = (tb + t) * 16 + xi;
-      uint32_t roff;
       if constexpr (L::tiled)
-        roff = (tb + t) < t_end ? (uint32_t)(tb + t) * tile_bytes + (uint32_t)(lane * 16) : kOOB;
+        roff[t] = (tb + t) < t_end ? (uint32_t)(tb + t) * tile_bytes + (uint32_t)(lane * 16) : kOOB;
       else
-        roff = ((tb + t) < t_end && x < p.n_rows) ? (uint32_t)((size_t)x * rb) : kOOB;
-      if constexpr (WT == MTP_W_Q4A32_TILED) {
-        // one KiB block per group quad: the chunk's four groups in one load
-        const uint32_t oob = s0 < nsteps ? 0u : kOOB;
-        const uint4 v = bload16_stream(wr, (roff | oob) + (uint32_t)(s0 / 4) * 1024u);
-        ck.w[t][0] = v.x; ck.w[t][1] = v.y; ck.w[t][2] = v.z; ck.w[t][3] = v.w;
-      } else {
+        roff[t] = ((tb + t) < t_end && x < p.n_rows) ? (uint32_t)((size_t)x * rb) : kOOB;
+    }
+    if constexpr (WT == MTP_W_Q4A32_TILED) {
+      // one KiB block per group quad: the chunk's four groups in one load
+      const uint32_t oob = s0 < nsteps ? 0u : kOOB;
 #pragma unroll
-        for (int u = 0; u < WU; ++u) {
-          const int s = s0 + u;
-          const uint32_t oob = s < nsteps ? 0u : kOOB;
+      for (int t = 0; t < WTV; ++t) {
+        const uint4 v = bload16_stream(wr, (roff[t] | oob) + (uint32_t)(s0 / 4) * 1024u);
+        ck.w[t][0] = v.x; ck.w[t][1] = v.y; ck.w[t][2] = v.z; ck.w[t][3] = v.w;
+      }
+    } else {
+      // K step outer: the chunk's first MFMAs need only the first WTV loads to have landed
+#pragma unroll
+      for (int u = 0; u < WU; ++u) {
+        const int s = s0 + u;
+        const uint32_t oob = s < nsteps ? 0u : kOOB;
+#pragma unroll
+        for (int t = 0; t < WTV; ++t) {
           if constexpr (WT == MTP_W_Q4A32)
-            ck.w[t][u] = bload4(wr, (roff | oob) + (uint32_t)((4 * s + g) * 4));
+            ck.w[t][u] = bload4(wr, (roff[t] | oob) + (uint32_t)((4 * s + g) * 4));
           else if constexpr (WT == MTP_W_BF16_TILED)
-            ck.w[t][u] = bload16_stream(wr, (roff | oob) + (uint32_t)s * 1024u);
+            ck.w[t][u] = bload16_stream(wr, (roff[t] | oob) + (uint32_t)s * 1024u);
           else
-            ck.w[t][u] = bload16(wr, (roff | oob) + (uint32_t)((4 * s + g) * 16));
+            ck.w[t][u] = bload16(wr, (roff[t] | oob) + (uint32_t)((4 * s + g) * 16));
         }
       }
-      if constexpr (L::q4) {
-        const uint32_t oob = s0 < nsteps ? 0u : kOOB;
+    }
+    if constexpr (L::q4) {
+      const uint32_t oob = s0 < nsteps ? 0u : kOOB;
+      // the chunk's 4 groups are one half of an octet of groups
+      const uint32_t step = L::tiled ? (uint32_t)(s0 / 8) * 256u + (uint32_t)(s0 & 4) * 2u : (uint32_t)(s0 * 2);
+#pragma unroll
+      for (int t = 0; t < WTV; ++t) {
         uint32_t so;
         if constexpr (L::tiled)   // block (tile, octet) of 256 B, 16 B per row
-          so = roff == kOOB ? kOOB : (roff - (uint32_t)(lane * 16)) / 8u + (uint32_t)(xi * 16);
+          so = roff[t] == kOOB ? kOOB : (roff[t] - (uint32_t)(lane * 16)) / 8u + (uint32_t)(xi * 16);
         else
-          so = roff == kOOB ? kOOB : (roff / (uint32_t)rb) * (uint32_t)(G32 * 2);
-        // the chunk's 4 groups are one half of an octet of groups
-        const uint32_t step = L::tiled ? (uint32_t)(s0 / 8) * 256u + (uint32_t)(s0 & 4) * 2u : (uint32_t)(s0 * 2);
+          so = roff[t] == kOOB ? kOOB : (roff[t] / (uint32_t)rb) * (uint32_t)(G32 * 2);
         ck.sc[t] = bload8(sr, (so | oob) + step);
         ck.mn[t] = bload8(mr, (so | oob) + step);
       }
