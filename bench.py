@@ -61,17 +61,23 @@ def parse():
                     help="keep the head row-major instead of repacking it once into the tiled layout")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (the HBM counter reference)")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn two rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json")
+    ap.add_argument("--summarize-counters", nargs=3, action="append", metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV"),
+                    help="turn the rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE) of a run of WORKLOAD into "
+                         "profiles/traffic.json (repeat once per workload)")
     return ap.parse_args()
 
 
 COPY_BYTES = 1 << 30
 
 
-def summarize_counters(fetch_csv: str, write_csv: str) -> None:
-    """Per-kernel HBM bytes per launch from rocprofv3 counter CSVs, scaled by the counters
-    of a plain copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES) in the same run."""
+KERNEL_KEYS = ("mtp_draft_head_kernel", "mtp_verify_logits_kernel", "mtp_verify_wide_kernel",
+               "mtp_verify_wide_merge_kernel", "mtp_accept_sample_kernel", "mtp_commit_state_kernel")
+
+
+def summarize_counters(runs) -> None:
+    """Per-kernel HBM bytes per launch from rocprofv3 counter CSVs, per workload, scaled by
+    the counters of a plain copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES) in the
+    same run."""
     import csv
     from collections import defaultdict
 
@@ -84,8 +90,6 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> None:
                 per[row["Kernel_Name"]].append(float(row["Counter_Value"]) * 1024.0)   # KiB -> B
         return per
 
-    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
-
     def copy_kernel(per):
         # the calibration copy is the multiply-by-one elementwise kernel over COPY_BYTES
         cands = [k for k in per if "elementwise" in k and "Mul" in k]
@@ -93,22 +97,21 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> None:
             raise SystemExit("no calibration copy kernel in the counter CSV (run bench.py --calibrate-copy)")
         return max(max(per[k]) for k in cands)
 
-    f_scale = COPY_BYTES / copy_kernel(fetch)
-    w_scale = COPY_BYTES / copy_kernel(write)
-    out = {"source_digest": source_digest(), "copy_bytes": COPY_BYTES,
-           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
-    for name in fetch:
-        short = None
-        for key in ("mtp_draft_head_kernel", "mtp_verify_logits_kernel", "mtp_accept_sample_kernel",
-                    "mtp_commit_state_kernel"):
-            if key in name:
-                short = key
-        if short is None or short in out["kernels"]:
-            continue
-        fb = float(np.median(fetch[name])) * f_scale
-        wb = float(np.median(write.get(name, [0.0]))) * w_scale
-        out["kernels"][short] = {"fetch_bytes": int(fb), "write_bytes": int(wb), "bytes_per_launch": int(fb + wb),
-                                 "launches": len(fetch[name]), "raw_kernel_name": name}
+    out = {"source_digest": source_digest(), "copy_bytes": COPY_BYTES, "workloads": {}}
+    for workload, fetch_csv, write_csv in runs:
+        fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+        f_scale = COPY_BYTES / copy_kernel(fetch)
+        w_scale = COPY_BYTES / copy_kernel(write)
+        wl = {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
+        for name in fetch:
+            short = next((key for key in KERNEL_KEYS if key + "<" in name or key + "(" in name), None)
+            if short is None or short in wl["kernels"]:
+                continue
+            fb = float(np.median(fetch[name])) * f_scale
+            wb = float(np.median(write.get(name, [0.0]))) * w_scale
+            wl["kernels"][short] = {"fetch_bytes": int(fb), "write_bytes": int(wb), "bytes_per_launch": int(fb + wb),
+                                    "launches": len(fetch[name]), "raw_kernel_name": name}
+        out["workloads"][workload] = wl
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
@@ -122,7 +125,7 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, units_per_launch: float):
+def load_traffic(workload: str, kernel: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
     try:
         t = json.load(open(TRAFFIC_FILE))
@@ -130,7 +133,7 @@ def load_traffic(kernel: str, units_per_launch: float):
         return None
     if t.get("source_digest") != source_digest():
         return None
-    k = t.get("kernels", {}).get(kernel)
+    k = t.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel)
     if not k:
         return None
     return k.get("bytes_per_launch")
@@ -139,7 +142,7 @@ def load_traffic(kernel: str, units_per_launch: float):
 def main():
     args = parse()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(args.summarize_counters)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -269,7 +272,7 @@ def main():
 
     def roof(bytes_per_launch, avg_s, kernel, flops=None):
         ach = bytes_per_launch / avg_s / 1e9
-        tr = load_traffic(kernel, 1)
+        tr = load_traffic(args.workload, kernel)
         r = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
              "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": tr,
              "kernel": kernel, "avg_launch_us": round(avg_s * 1e6, 2),

@@ -36,10 +36,16 @@ using namespace lm;
 // Tuning knobs (compile-time): tiles per wave pass, K steps per prefetch chunk, the grid
 // cap, and the waves per SIMD the register budget is sized for.
 #ifndef MTP_LM_TV
-#define MTP_LM_TV 2
+#define MTP_LM_TV 1
 #endif
 #ifndef MTP_LM_U
 #define MTP_LM_U 8
+#endif
+#ifndef MTP_LM_TV_Q4
+#define MTP_LM_TV_Q4 2
+#endif
+#ifndef MTP_LM_U_Q4
+#define MTP_LM_U_Q4 8
 #endif
 #ifndef MTP_LM_MAX_GRID
 #define MTP_LM_MAX_GRID 256
@@ -49,8 +55,10 @@ using namespace lm;
 #endif
 
 constexpr int kWaves = kLmheadThreads / 64;
-constexpr int TV = MTP_LM_TV;   // 16-row vocabulary tiles per wave per pass
-constexpr int U = MTP_LM_U;     // K steps per prefetch chunk
+constexpr int kTV = MTP_LM_TV;       // 16-row vocabulary tiles per wave per pass
+constexpr int kU = MTP_LM_U;         // K steps per prefetch chunk
+constexpr int kTVQ4 = MTP_LM_TV_Q4;  // the same for 4-bit heads, whose K steps carry a
+constexpr int kUQ4 = MTP_LM_U_Q4;    // quarter of the bytes
 constexpr int kMaxGrid = MTP_LM_MAX_GRID;
 
 template <int WT, bool SAMPLED, bool VERIFY>
@@ -61,6 +69,9 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   const int xi = lane & 15, g = lane >> 4;
   const int M = p.M, d = p.d;
   using L = Layout<WT>;
+  constexpr int TV = L::q4 ? kTVQ4 : kTV;
+  constexpr int U = L::q4 ? kUQ4 : kU;
+  static_assert(!L::q4 || U % 8 == 0, "4-bit chunks cover whole octets of groups (one scale vector each)");
   const int nsteps = L::f32 ? d / 16 : d / 32;
   // chunks per tile group, rounded up to even for the two-buffer pipeline (a chunk past
   // the end reads out of range, i.e. zeros, and its MFMAs add +0)
@@ -108,7 +119,7 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   typedef typename std::conditional<L::q4, uint32_t, uint4>::type WFrag;
   struct Chunk {
     WFrag w[TV][U];
-    uint4 sc[TV], mn[TV];   // 4-bit heads: scales and mins of the chunk's U groups
+    uint4 sc[TV][(U + 7) / 8], mn[TV][(U + 7) / 8];   // 4-bit heads: scales and mins, 8 groups each
   };
   auto load = [&](Chunk& ck, const uint32_t (&roff)[TV], int s0) {
 #pragma unroll
@@ -135,15 +146,19 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
         }
       }
       if constexpr (L::q4) {
-        const uint32_t oob = s0 < nsteps ? 0u : kOOB;
         uint32_t so;
         if constexpr (L::tiled)   // block (tile, octet) of 256 B, 16 B per row
           so = roff[t] == kOOB ? kOOB : (roff[t] - (uint32_t)(lane * 16)) / 8u + (uint32_t)(xi * 16);
         else
           so = roff[t] == kOOB ? kOOB : (roff[t] / (uint32_t)rb) * (uint32_t)(G32 * 2);
-        const uint32_t step = L::tiled ? (uint32_t)(s0 / 8) * 256u : (uint32_t)(s0 * 2);
-        ck.sc[t] = bload16(sr, (so | oob) + step);
-        ck.mn[t] = bload16(mr, (so | oob) + step);
+#pragma unroll
+        for (int o = 0; o < (U + 7) / 8; ++o) {
+          const int s = s0 + 8 * o;
+          const uint32_t oob = s < nsteps ? 0u : kOOB;
+          const uint32_t step = L::tiled ? (uint32_t)(s / 8) * 256u : (uint32_t)(s * 2);
+          ck.sc[t][o] = bload16(sr, (so | oob) + step);
+          ck.mn[t][o] = bload16(mr, (so | oob) + step);
+        }
       }
     }
   };
@@ -176,8 +191,10 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
           for (int t = 0; t < TV; ++t) {
             const f32x4 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 as_bf16x8(a), as_bf16x8(q4_expand(ck.w[t][u])), f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-            const uint32_t sw = (u < 2) ? ck.sc[t].x : (u < 4) ? ck.sc[t].y : (u < 6) ? ck.sc[t].z : ck.sc[t].w;
-            const uint32_t mw = (u < 2) ? ck.mn[t].x : (u < 4) ? ck.mn[t].y : (u < 6) ? ck.mn[t].z : ck.mn[t].w;
+            const uint4 sq = ck.sc[t][u / 8], mq = ck.mn[t][u / 8];
+            const int uo = u % 8;
+            const uint32_t sw = (uo < 2) ? sq.x : (uo < 4) ? sq.y : (uo < 6) ? sq.z : sq.w;
+            const uint32_t mw = (uo < 2) ? mq.x : (uo < 4) ? mq.y : (uo < 6) ? mq.z : mq.w;
             const float sv = bf16_to_f32((uint16_t)((u & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
             const float mv = bf16_to_f32((uint16_t)((u & 1) ? (mw >> 16) : (mw & 0xFFFFu)));
             const float off = mv - 128.0f * sv;
@@ -189,15 +206,12 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
     }
   };
 
-  // the first chunk's weight loads are in flight while the hidden rows are staged
-  Chunk A, B;
-  uint32_t roff_cur[TV], roff_nxt[TV];
-  row_offsets(t_begin, roff_cur);
-  load(A, roff_cur, 0);
-
-  // ---- stage the hidden rows as A-operand fragments -------------------------------
+  // ---- stage the hidden rows as A-operand fragments, with the first weight chunk in
+  //      flight.  Loads retire in issue order: the hidden loads go out first and all
+  //      together (up to kPreFrags per thread, which covers d = 2560 at 16 rows), so
+  //      writing them to LDS waits for neither the weights nor a chain of round trips.
   const int nfrag = nsteps * 4 * M;
-  for (int f = tid; f < nfrag; f += kLmheadThreads) {
+  auto hfrag = [&](int f) {
     const int i = f % M, sg = f / M, gg = sg & 3, s = sg >> 2;
     uint4 v;
     if (L::f32) {
@@ -206,8 +220,21 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
       v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.hidden) + (size_t)i * d + 32 * s + 8 * gg);
       if (L::q4) v = q4_order(v);
     }
-    frag[f] = v;
-  }
+    return v;
+  };
+  constexpr int kPreFrags = 10;
+  uint4 hv[kPreFrags];
+#pragma unroll
+  for (int q = 0; q < kPreFrags; ++q)
+    if (tid + q * kLmheadThreads < nfrag) hv[q] = hfrag(tid + q * kLmheadThreads);
+  Chunk A, B;
+  uint32_t roff_cur[TV], roff_nxt[TV];
+  row_offsets(t_begin, roff_cur);
+  load(A, roff_cur, 0);
+#pragma unroll
+  for (int q = 0; q < kPreFrags; ++q)
+    if (tid + q * kLmheadThreads < nfrag) frag[tid + q * kLmheadThreads] = hv[q];
+  for (int f = tid + kPreFrags * kLmheadThreads; f < nfrag; f += kLmheadThreads) frag[f] = hfrag(f);
   if (L::q4) {
     // per 32-value group and hidden row: sum of the hidden values
     for (int e = tid; e < nsteps * 16; e += kLmheadThreads) {
@@ -280,6 +307,7 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   // ---- reduce: 16 lanes of a row group, then the block's waves -------------------
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
+    if (!rvalid[r]) continue;   // uniform over the 16 lanes the butterfly reads
     rowacc_merge(acc[r], rowacc_xor16<1>(acc[r]));
     rowacc_merge(acc[r], rowacc_xor16<2>(acc[r]));
     rowacc_merge(acc[r], rowacc_xor16<4>(acc[r]));
@@ -309,18 +337,31 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   __syncthreads();
   if (!*last_flag) return;
 
-  // ---- last block: one wave per row merges the per-block partials in block order ---
-  for (int j = wave; j < M; j += kWaves) {
-    RowAcc part[kMaxGrid / 64];
+  // ---- last block: one wave per row merges the per-block partials in block order.
+  //      These loads bypass the caches and each round trip is long, so every load a wave
+  //      needs (the partials of its rows, the drafted-id logits) goes out before the first
+  //      merge.  M <= kLmheadMaxRows, so a wave has at most kRowsPerWave rows.
+  constexpr int kRowsPerWave = (kLmheadMaxRows + kWaves - 1) / kWaves;
+  RowAcc part[kRowsPerWave][kMaxGrid / 64];
+  uint32_t zbits[kRowsPerWave];
+#pragma unroll
+  for (int jj = 0; jj < kRowsPerWave; ++jj) {
+    const int j = wave + jj * kWaves;
 #pragma unroll
     for (int q = 0; q < kMaxGrid / 64; ++q) {
       const int blk = lane + 64 * q;
-      if (blk < G) part[q] = load_partial(pr, (uint32_t)(((size_t)blk * M + j) * sizeof(RowAcc)));
-      else rowacc_init(part[q]);
+      if (j < M && blk < G) part[jj][q] = load_partial(pr, (uint32_t)(((size_t)blk * M + j) * sizeof(RowAcc)));
+      else rowacc_init(part[jj][q]);
     }
-    RowAcc a = part[0];
+    zbits[jj] = (VERIFY && j < M) ? load_coherent(reinterpret_cast<const uint32_t*>(ztok) + j) : 0u;
+  }
 #pragma unroll
-    for (int q = 1; q < kMaxGrid / 64; ++q) rowacc_merge(a, part[q]);
+  for (int jj = 0; jj < kRowsPerWave; ++jj) {
+    const int j = wave + jj * kWaves;
+    if (j >= M) continue;   // wave-uniform
+    RowAcc a = part[jj][0];
+#pragma unroll
+    for (int q = 1; q < kMaxGrid / 64; ++q) rowacc_merge(a, part[jj][q]);
 #pragma unroll
     for (int mask = 1; mask < 64; mask <<= 1) {
       const RowAcc o = rowacc_shfl_xor(a, mask);
@@ -332,9 +373,8 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
       if (VERIFY) {
         const int b = j / p.rows_per_req, i = j % p.rows_per_req;
         const int t = (i < p.k) ? p.drafts[(size_t)b * p.k_max + i] : -1;
-        st.z_tok = (t >= 0 && t < p.n_rows && !(fl & MTP_ROW_INVALID))
-                       ? sanitize(__uint_as_float(load_coherent(reinterpret_cast<const uint32_t*>(ztok) + j)), fl)
-                       : kNegInf;
+        st.z_tok = (t >= 0 && t < p.n_rows && !(fl & MTP_ROW_INVALID)) ? sanitize(__uint_as_float(zbits[jj]), fl)
+                                                                         : kNegInf;
       } else {
         st.z_tok = (fl & MTP_ROW_POSINF) ? 0.0f : ((fl & MTP_ROW_INVALID) ? kNegInf : (SAMPLED ? a.gz : a.zmax));
         p.tokens[(size_t)j * p.k_max + p.row_base] = st.sample;
