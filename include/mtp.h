@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MTP_ABI_VERSION 1
+#define MTP_ABI_VERSION 2
 
 /* ---------------------------------------------------------------------------------- */
 /* status codes                                                                        */
@@ -111,15 +111,36 @@ typedef struct mtp_head {
 /* Random draws use Philox4x32-10 (Salmon et al., SC'11): key = (seed lo32, seed hi32),
  * counter = (x >> 2, stream << 8 | row, request_base + b, cycle), word x & 3, where x is
  * the vocabulary id (0 for the acceptance uniform).  Streams: 0 draft sample, 1
- * acceptance uniform, 2 correction/bonus sample.  Uniforms: acceptance
- * u = ((w >> 8) + 1) * 2^-24 in (0, 1]; Gumbel u = (2 (w >> 9) + 1) * 2^-24 in (0, 1),
- * noise -ln(-ln u).  Every categorical draw is argmax(z/T + noise), lowest id on ties. */
+ * acceptance uniform, 2 correction/bonus sample, 3 the trunk's own sample under
+ * exact-match acceptance, whose counter is (x >> 2, 3 << 8, request_base + b, position):
+ * keyed by the absolute position of the token, not by the cycle or the row.  Uniforms:
+ * acceptance u = ((w >> 8) + 1) * 2^-24 in (0, 1]; Gumbel u = (2 (w >> 9) + 1) * 2^-24
+ * in (0, 1), noise -ln(-ln u).  Every categorical draw is argmax(z/T + noise), lowest id
+ * on ties. */
+typedef enum mtp_accept_rule {
+  /* T > 0: u*q <= p with the residual resample (DS4Server issue above, closing comment
+   * "Review"): the output follows p, but it is not the token sequence of decoding
+   * without speculation */
+  MTP_ACCEPT_RATIO = 0,
+  /* T > 0: a draft is accepted only if it equals the token the trunk samples at that
+   * position (lucebox-hub PR above, sections "Exactness" and "Notes"): with the trunk's
+   * draws keyed by position (stream 3), the output is the token sequence of decoding
+   * without speculation under the same seed.  Drafts are the draft head's argmax. */
+  MTP_ACCEPT_EXACT = 1
+} mtp_accept_rule;
+
 typedef struct mtp_sampling {
   float temperature;     /* T >= 0; 0 = greedy (argmax drafts, exact-match acceptance) */
   int32_t eos_id;        /* end-of-sequence id, or -1 for none                          */
   uint64_t seed;         /* Philox key                                                  */
   uint32_t cycle;        /* cycle counter; a new value gives fresh draws                */
   uint32_t request_base; /* counter index of request 0 of this call                     */
+  int32_t accept_rule;   /* mtp_accept_rule; no effect at T = 0                          */
+  int32_t reserved;      /* must be 0                                                   */
+  const int32_t* positions; /* device int32 [B], read by mtp_verify_logits under
+                             * MTP_ACCEPT_EXACT at T > 0 (else may be NULL): absolute
+                             * position of the token verify row 0 of request b predicts;
+                             * row i samples position positions[b] + i                  */
 } mtp_sampling;
 
 /* ---------------------------------------------------------------------------------- */
@@ -174,12 +195,14 @@ size_t mtp_workspace_bytes(int32_t op, int32_t rows, int32_t n_vocab_rows, int32
  * a 64,000-row draft head, token picked on the GPU and fed from device memory).
  *   z[b][x] = sum_j W[x][j] * hidden[b][j]   for x < n_draft   (fp32 accumulation)
  *   T = 0: token = lowest-id argmax of z;  T > 0: token = argmax(z/T + Gumbel(stream 0,
- *   row = slot)), a sample of q = softmax(z/T) over the first n_draft ids.
+ *   row = slot)), a sample of q = softmax(z/T) over the first n_draft ids.  Under
+ *   MTP_ACCEPT_EXACT the draft head works as at T = 0 (argmax, statistics at T_eff = 1).
  * hidden:        [B][d] in htype.
  * draft_tokens:  int32 [B][k_max]; writes column `slot`; -1 for an all -inf row.
  * draft_stats:   mtp_row_stats [B][k_max]; writes column `slot`.
  * draft_logits:  float [B][k_max][n_draft] raw (unsanitised) logits, writes slot `slot`;
- *                required when T > 0 (the residual needs q), may be NULL at T = 0.
+ *                required when T > 0 under MTP_ACCEPT_RATIO (the residual needs q), else
+ *                may be NULL.
  * 1 <= n_draft <= vocab; 1 <= B <= 16; 0 <= slot < k_max <= 7.                        */
 int mtp_draft_head(const mtp_head* head, int32_t n_draft, const void* hidden, int32_t htype,
                    int32_t B, int32_t slot, int32_t k_max, const mtp_sampling* smp,
@@ -192,8 +215,12 @@ int mtp_draft_head(const mtp_head* head, int32_t n_draft, const void* hidden, in
  * B, k or the row's position in the batch).
  * hidden:        [B][k+1][d] in htype; row 0 = the last committed token, row i = draft d_i.
  * draft_tokens:  int32 [B][k_max]; row i < k records z at draft_tokens[b][i].
- * row_stats:     mtp_row_stats [B][k+1].
- * logits:        float [B][k+1][vocab] raw logits; required when T > 0, else may be NULL.
+ * row_stats:     mtp_row_stats [B][k+1].  At T > 0 `sample` is argmax(z/T + Gumbel) on
+ *                stream 2, row i, or under MTP_ACCEPT_EXACT on stream 3 at position
+ *                smp->positions[b] + i (the trunk's own sample, the same draw whatever the
+ *                cycle, row or batch the position is verified in).
+ * logits:        float [B][k+1][vocab] raw logits; required when T > 0 under
+ *                MTP_ACCEPT_RATIO, else may be NULL.
  * 1 <= k <= k_max <= 7; 1 <= B*(k+1) <= 128.                                           */
 int mtp_verify_logits(const mtp_head* head, const void* hidden, int32_t htype, int32_t B,
                       int32_t k, const int32_t* draft_tokens, int32_t k_max,
@@ -204,16 +231,20 @@ int mtp_verify_logits(const mtp_head* head, const void* hidden, int32_t htype, i
  *   a target row i that is all -inf stops the block before it (MTP_ACC_ROW_INVALID,
  *   n_emit = n_accept = i, no further token);
  *   T = 0: accepted iff t == argmax of verify row i (lucebox-hub PR, "Exactness");
- *   T > 0: accepted iff p_i(t) > 0 and u*q_i(t) <= p_i(t), u from stream 1 (DS4Server
- *          issue, closing comment "Review"); q is 0 outside the draft vocabulary;
- *   at the first rejection the next token is y_i (T = 0) or a draw from
- *   max(0, p_i - q_i) renormalised (Gumbel-max on stream 2, row i); an empty residual
- *   draws from p_i instead (MTP_ACC_RESID_FALLBACK);
+ *   T > 0, MTP_ACCEPT_RATIO: accepted iff p_i(t) > 0 and u*q_i(t) <= p_i(t), u from
+ *          stream 1 (DS4Server issue, closing comment "Review"); q is 0 outside the draft
+ *          vocabulary;
+ *   T > 0, MTP_ACCEPT_EXACT: accepted iff t == the sample of verify row i (lucebox-hub
+ *          PR, "Exactness");
+ *   at the first rejection the next token is y_i (T = 0), the sample of row i
+ *   (MTP_ACCEPT_EXACT), or a draw from max(0, p_i - q_i) renormalised (Gumbel-max on
+ *   stream 2, row i); an empty residual draws from p_i instead (MTP_ACC_RESID_FALLBACK);
  *   an accepted t == eos_id ends the block with EOS as its last token (DS4Server issue,
  *   "Implementation": nothing is kept beyond EOS); n_accept = i;
  *   all k accepted: a bonus token from row k (argmax, or the stream-2 sample).
  * Inputs are the outputs of the draft and verify calls of the same cycle (draft_logits
- * and logits are read only when T > 0).  vocab and n_draft must match those calls.
+ * and logits are read only when T > 0 under MTP_ACCEPT_RATIO).  vocab and n_draft must
+ * match those calls.
  * out_tokens: int32 [B][k+1] = d_1..d_a, last, then -1;  n_accept, n_emit: int32 [B]
  * (n_emit = n_accept + 1 except with MTP_ACC_ROW_INVALID);  flags: uint32 [B].        */
 int mtp_accept_sample(int32_t B, int32_t k, int32_t k_max, int32_t vocab, int32_t n_draft,

@@ -38,7 +38,10 @@ Readings where the pages are silent (each is a stated choice, listed with the de
   * drafts at T > 0 are samples from q at the same T (Gumbel-max);
   * every categorical draw is Gumbel-max on Philox4x32-10 words; counter =
     (x >> 2, stream << 8 | row, request, cycle), key = (seed lo32, seed hi32), word x & 3;
-    streams: 0 draft, 1 acceptance uniform, 2 correction/bonus;
+    streams: 0 draft, 1 acceptance uniform, 2 correction/bonus, 3 the trunk's own sample
+    under exact-match acceptance, whose counter is (x >> 2, 3 << 8, request, position):
+    the same draw for a position in whatever cycle or row it is verified;
+  * exact-match acceptance at T > 0 takes the drafts as the draft head's argmax;
   * all k drafts accepted -> one bonus token from row k;
   * an accepted EOS draft ends the block: n_accept = its row, the EOS is the last token
     and is never consumed, so snapshot n_accept is committed;
@@ -68,7 +71,8 @@ ACC_NONFINITE_TARGET = 1 << 4
 ACC_NONFINITE_DRAFT = 1 << 5
 ACC_DRAFT_INVALID = 1 << 6
 
-STREAM_DRAFT, STREAM_ACCEPT, STREAM_RESAMPLE = 0, 1, 2
+STREAM_DRAFT, STREAM_ACCEPT, STREAM_RESAMPLE, STREAM_TRUNK = 0, 1, 2, 3
+RULE_RATIO, RULE_EXACT = "ratio", "exact"
 
 NEG_INF = -np.inf
 F32 = np.float32
@@ -133,6 +137,24 @@ def gumbel_noise(seed: int, stream: int, row, b, cycle: int, n: int) -> np.ndarr
     row = np.asarray(row)[..., None]
     u = uniform_gumbel(philox_words(seed, stream, row, b, cycle, np.arange(n)))
     return -np.log(-np.log(u))
+
+
+def trunk_noise(seed: int, b: int, position: int, n: int) -> np.ndarray:
+    """Gumbel noise of the trunk's own draw for request b at an absolute position.
+
+    Exact-match acceptance [MTP-PR "Exactness", "Notes"] keeps a draft only if it equals
+    the token the trunk samples, so that the output is the token sequence of decoding
+    without speculation: that draw must depend on the position alone, never on the cycle
+    or the verify row.  Stream 3, counter (x >> 2, 3 << 8, b, position).
+    """
+    return gumbel_noise(seed, STREAM_TRUNK, 0, b, int(position) & 0xFFFFFFFF, n)
+
+
+def trunk_sample(z_row: np.ndarray, T: float, seed: int, b: int, position: int):
+    """The trunk's token at one position: argmax(z/T + trunk noise), lowest id on ties,
+    decided in fp32; also the fp64 top-2 gap of the scores.  z_row is sanitised."""
+    G = trunk_noise(seed, b, position, z_row.shape[-1])
+    return int(argmax_lowest_f32(_f32_add(z_row / T, G))), float(top2_gap(z_row / T + G))
 
 
 # ----------------------------------------------------------------------------------
@@ -265,12 +287,14 @@ def draft_rows(W64: np.ndarray, n_draft: int, h: np.ndarray, T: float, seed: int
 # O4  verify rows
 # ----------------------------------------------------------------------------------
 def verify_rows(W64: np.ndarray, h_v: np.ndarray, drafts, T: float, seed: int, cycle: int,
-                delta: float, b_ids=None) -> dict:
+                delta: float, b_ids=None, positions=None) -> dict:
     """Full-vocabulary logits of the k+1 verify rows of every request [MTP-PR "What"].
 
     h_v [B][k+1][d]; drafts [B][k] (row i is checked against drafts[:, i]).  Per row:
     lowest-id argmax y, the Gumbel-max sample at T from stream 2 (the bonus token at row
-    k), max and lse of the sanitised z/T, and the sanitised logit at the drafted id.
+    k) -- or, when ``positions`` [B] is given (exact-match acceptance), the trunk's own
+    sample at position positions[b] + i --, max and lse of the sanitised z/T, and the
+    sanitised logit at the drafted id.
     """
     B, K1, _ = h_v.shape
     b_ids = np.arange(B) if b_ids is None else np.asarray(b_ids)
@@ -279,7 +303,15 @@ def verify_rows(W64: np.ndarray, h_v: np.ndarray, drafts, T: float, seed: int, c
     zs, rflags = sanitize(z)
     y = argmax_lowest_f32(zs)
     y_margin = top2_gap(zs)
-    if T > 0:
+    if T > 0 and positions is not None:
+        sample = np.empty((B, K1), dtype=np.int64)
+        s_margin = np.empty((B, K1))
+        for bi in range(B):
+            for i in range(K1):
+                sample[bi, i], s_margin[bi, i] = trunk_sample(zs[bi, i], T, seed, int(b_ids[bi]),
+                                                              int(positions[bi]) + i)
+        sample = np.where((rflags & ROW_INVALID) != 0, -1, sample)
+    elif T > 0:
         G = gumbel_noise(seed, STREAM_RESAMPLE, np.arange(K1)[None, :], b_ids[:, None], cycle, V)
         sample = argmax_lowest_f32(_f32_add(zs / T, G))
         s_margin = top2_gap(zs / T + G)
@@ -320,7 +352,7 @@ def residual_log_weights(lp: np.ndarray, lq: np.ndarray) -> np.ndarray:
 
 
 def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int, eos: int,
-           delta: float, b_ids=None, draft_near_tie=None) -> dict:
+           delta: float, b_ids=None, draft_near_tie=None, rule: str = RULE_RATIO, target=None) -> dict:
     """O5 for B requests: scan the drafts, stop at the first rejection, emit one more token.
 
     drafts [B][k]; zd_raw [B][k][n_draft] raw draft logits (needed when T > 0);
@@ -332,6 +364,9 @@ def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int
               rejection the token is drawn from max(0, p_i - q_i) renormalised (Gumbel-max on
               stream 2) [DS4-98 "Implementation", closing comment "Review"]; the residual is
               empty only when p = q, then it is drawn from p (flag RESID_FALLBACK).
+      T >  0, rule "exact": accepted iff it equals the trunk's own sample at row i, and
+              that sample is also the token after the last accepted draft [MTP-PR
+              "Exactness", "Notes"]; ``target`` is verify_rows' output with positions.
       An accepted EOS draft ends the block [DS4-98 "Implementation"]; an all -inf target
       row stops the block before it with no extra token.
     Returns tokens [B][k+1] (-1 padded), n_accept, n_emit, flags, and the first row whose
@@ -346,12 +381,15 @@ def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int
     lse_v = logsumexp_rows(zv / Te)
     y = argmax_lowest_f32(zv)
     y_margin = top2_gap(zv)
+    exact = T > 0 and rule == RULE_EXACT
+    if exact:
+        ys, ys_margin = np.asarray(target["sample"]), np.asarray(target["s_margin"])
     if zd_raw is not None:
         # draft-row flags are reported at any temperature; q itself is used only when T > 0
         zd, dflags = sanitize(zd_raw)
         lse_d = logsumexp_rows(zd / Te)
-    elif T > 0:
-        raise ValueError("sampled acceptance needs the draft logits")
+    elif T > 0 and not exact:
+        raise ValueError("the ratio test needs the draft logits")
     else:
         dflags = np.zeros((B, k), dtype=np.uint32)
 
@@ -385,7 +423,10 @@ def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int
         t_ok = (t >= 0) & (t < V)
         flags[active & ~t_ok] |= ACC_DRAFT_INVALID
         tc = np.clip(t, 0, V - 1)
-        if T > 0:
+        if exact:
+            ok = t_ok & (t == ys[:, i])
+            mark_tie(active & (ys_margin[:, i] <= delta / T), i)
+        elif T > 0:
             lp_t = np.where(t_ok, zv[rows, i, tc] / T - lse_v[:, i], NEG_INF)
             in_draft = t_ok & (t < n_draft) & ((dflags[:, i] & ROW_INVALID) == 0)
             with np.errstate(invalid="ignore"):
@@ -428,6 +469,9 @@ def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int
         if T <= 0:
             last[sel] = y[sel, a]
             continue
+        if exact:
+            last[sel] = ys[sel, a]
+            continue
         lp = zv[sel, a] / T - lse_v[sel, a][:, None]
         lq = np.full((sel.size, V), NEG_INF)
         dval = (dflags[sel, a] & ROW_INVALID) == 0
@@ -455,7 +499,10 @@ def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int
     sel = np.nonzero(stop_kind == 2)[0]
     flags[sel] |= ACC_ALL_ACCEPTED
     if sel.size:
-        if T > 0:
+        if exact:
+            last[sel] = ys[sel, k]
+            mark_tie(np.isin(rows, sel[ys_margin[sel, k] <= delta / T]), k)
+        elif T > 0:
             G = gumbel_noise(seed, STREAM_RESAMPLE, k, b_ids[sel], cycle, V)
             last[sel], gap = gumbel_pick(zv[sel, k] / T, G)
             mark_tie(np.isin(rows, sel[gap <= delta / T]), k)
@@ -509,20 +556,26 @@ def commit(snapshots: np.ndarray, live: np.ndarray, kv: np.ndarray, kv_len: np.n
 # one whole cycle
 # ----------------------------------------------------------------------------------
 def cycle(W64: np.ndarray, n_draft: int, h_d: np.ndarray, h_v: np.ndarray, T: float,
-          seed: int, cycle_id: int, eos: int, delta: float, drafts=None) -> dict:
+          seed: int, cycle_id: int, eos: int, delta: float, drafts=None, rule: str = RULE_RATIO,
+          positions=None) -> dict:
     """k draft-head calls, one verify over k+1 rows, acceptance [MTP-PR "What"].
 
     h_d [B][k][d], h_v [B][k+1][d] in fp64.  ``drafts`` overrides the draft head's picks
-    (the draft logits are still computed, since q is needed for the ratio test).
+    (the draft logits are still computed, since q is needed for the ratio test).  Rule
+    "exact" (T > 0) takes argmax drafts and needs ``positions`` [B], the absolute position
+    verify row 0 of each request predicts.
     """
     B, k, _ = h_d.shape
-    dr = [draft_rows(W64, n_draft, h_d[:, i], T, seed, i, cycle_id, delta) for i in range(k)]
+    exact = T > 0 and rule == RULE_EXACT
+    Td = 0.0 if exact else T
+    dr = [draft_rows(W64, n_draft, h_d[:, i], Td, seed, i, cycle_id, delta) for i in range(k)]
     picked = np.stack([r["token"] for r in dr], axis=1)
     use = picked if drafts is None else np.asarray(drafts, dtype=np.int64)
     dnt = np.stack([r["near_tie"] for r in dr], axis=1)
     if drafts is not None:
         dnt[:] = False
-    vr = verify_rows(W64, h_v, use, T, seed, cycle_id, delta)
+    vr = verify_rows(W64, h_v, use, T, seed, cycle_id, delta, positions=positions if exact else None)
     zd = np.stack([r["logits"] for r in dr], axis=1)
-    acc = accept(use, zd, vr["logits"], n_draft, T, seed, cycle_id, eos, delta, draft_near_tie=dnt)
+    acc = accept(use, zd, vr["logits"], n_draft, T, seed, cycle_id, eos, delta, draft_near_tie=dnt,
+                 rule=rule, target=vr)
     return dict(drafts=use, draft=dr, verify=vr, accept=acc)

@@ -1,7 +1,10 @@
 // Acceptance, first rejection, residual resample and EOS truncation for B requests.
 //
 // Greedy (T = 0): a draft is accepted only if it equals the verify row's argmax
-// (lucebox-hub PR "feat(qwen4exp): MTP speculative decoding", section "Exactness").
+// (lucebox-hub PR "feat(qwen4exp): MTP speculative decoding", section "Exactness"); with
+// exact-match acceptance at T > 0 (same PR, "Exactness" and "Notes") it must equal the
+// verify row's sample, the trunk's own position-keyed draw, which is also the token
+// emitted at the first rejection and after the last draft.
 // Sampled (T > 0): draft t is accepted iff p(t) > 0 and u * q(t) <= p(t); at the first
 // rejection the next token is drawn from max(0, p - q) renormalised (DS4Server issue
 // "Add Qwen3.8 Flash Next native MTP speculation", section "Implementation" and closing
@@ -66,8 +69,8 @@ __device__ Chain walk_chain(const AcceptLaunch& p, int b, float inv_t) {
     const bool t_ok = t >= 0 && t < p.vocab;
     if (!t_ok) c.flags |= MTP_ACC_DRAFT_INVALID;
     bool ok;
-    if (!sampled) {
-      ok = t_ok && t == vs.argmax;
+    if (!sampled || p.exact) {
+      ok = t_ok && t == (sampled ? vs.sample : vs.argmax);
     } else if (!t_ok) {
       ok = false;
     } else {
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(kAcceptThreads) void mtp_accept_sample_kernel(Accep
   const int K1 = p.k + 1;
 
   Chain c = walk_chain(p, b, inv_t);
-  const bool resample = sampled && c.kind == kRejected;
+  const bool resample = sampled && !p.exact && c.kind == kRejected;
 
   // ---- residual slice: best ln r(x) + Gumbel(x) over x in this block's range ------
   float best = kNegInf;
@@ -205,6 +208,8 @@ __global__ __launch_bounds__(kAcceptThreads) void mtp_accept_sample_kernel(Accep
     const mtp_row_stats vs = p.vstats[(size_t)b * K1 + c.a];
     if (!sampled) {
       c.last = vs.argmax;
+    } else if (p.exact) {
+      c.last = vs.sample;   // the trunk's own sample at this position
     } else if (mass) {
       c.last = best_idx;
     } else {
@@ -230,20 +235,20 @@ __global__ __launch_bounds__(kAcceptThreads) void mtp_accept_sample_kernel(Accep
 
 }  // namespace
 
-int accept_slices(int vocab, float temperature) {
-  if (!(temperature > 0.0f)) return 1;
+int accept_slices(int vocab, bool residual) {
+  if (!residual) return 1;
   int s = (vocab + kSliceElems - 1) / kSliceElems;
   return s < 1 ? 1 : (s > kMaxSlices ? kMaxSlices : s);
 }
 
-size_t accept_ws_bytes(int B, int vocab, float temperature) {
-  const int S = accept_slices(vocab, temperature);
+size_t accept_ws_bytes(int B, int vocab, bool residual) {
+  const int S = accept_slices(vocab, residual);
   if (S <= 1) return 0;
   return (((size_t)B * 4 + 255) / 256) * 256 + (size_t)B * S * sizeof(SlicePartial);
 }
 
 hipError_t launch_accept(const AcceptLaunch& p, hipStream_t stream) {
-  const int S = accept_slices(p.vocab, p.temperature);
+  const int S = accept_slices(p.vocab, p.temperature > 0.0f && !p.exact);
   hipLaunchKernelGGL(mtp_accept_sample_kernel, dim3(p.B, S), dim3(kAcceptThreads), 0, stream, p);
   return hipGetLastError();
 }

@@ -45,8 +45,13 @@ int check_sampling(const mtp_sampling* s) {
   if (!s) return MTP_ERR_NULL;
   if (!(s->temperature >= 0.0f) || !isfinite(s->temperature)) return MTP_ERR_RANGE;
   if (s->eos_id < -1) return MTP_ERR_RANGE;
+  if (s->accept_rule != MTP_ACCEPT_RATIO && s->accept_rule != MTP_ACCEPT_EXACT) return MTP_ERR_RANGE;
+  if (s->reserved != 0) return MTP_ERR_RANGE;
   return MTP_OK;
 }
+
+// T > 0 with the ratio test: draws from q and p (draft logits, residual)
+bool ratio_sampling(const mtp_sampling* s) { return s->temperature > 0.0f && s->accept_rule == MTP_ACCEPT_RATIO; }
 
 float inv_t_eff(float t) { return t > 0.0f ? 1.0f / t : 1.0f; }
 
@@ -80,7 +85,7 @@ size_t mtp_workspace_bytes(int32_t op, int32_t rows, int32_t n_vocab_rows, int32
     case MTP_OP_ACCEPT:
       if (B < 1 || n_vocab_rows < 1) return 0;
       // sized for sampled acceptance (greedy needs none)
-      return accept_ws_bytes(B, n_vocab_rows, 1.0f) + 256;
+      return accept_ws_bytes(B, n_vocab_rows, true) + 256;
     default:
       return 0;
   }
@@ -121,7 +126,7 @@ int mtp_draft_head(const mtp_head* head, int32_t n_draft, const void* hidden, in
   if (B < 1 || B > kLmheadMaxRows) return MTP_ERR_SHAPE;
   if (k_max < 1 || k_max > kMaxK) return MTP_ERR_SHAPE;
   if (slot < 0 || slot >= k_max) return MTP_ERR_RANGE;
-  const bool sampled = smp->temperature > 0.0f;
+  const bool sampled = ratio_sampling(smp);   // exact-match acceptance drafts the argmax
   if (sampled && !draft_logits) return MTP_ERR_NULL;
   if (!aligned16(hidden) || !aligned16(draft_stats) || (draft_logits && !aligned16(draft_logits)))
     return MTP_ERR_ALIGN;
@@ -146,7 +151,8 @@ int mtp_draft_head(const mtp_head* head, int32_t n_draft, const void* hidden, in
   p.key1 = (uint32_t)(smp->seed >> 32);
   p.cycle = smp->cycle;
   p.request_base = smp->request_base;
-  p.inv_t = inv_t_eff(smp->temperature);
+  p.positions = nullptr;
+  p.inv_t = inv_t_eff(sampled ? smp->temperature : 0.0f);
   p.sampled = sampled;
   p.verify = 0;
   p.drafts = nullptr;
@@ -176,8 +182,11 @@ int mtp_verify_logits(const mtp_head* head, const void* hidden, int32_t htype, i
   if (M > kLmheadMaxWideRows) return MTP_ERR_SHAPE;
   const bool wide = M > kLmheadMaxRows;
   const bool sampled = smp->temperature > 0.0f;
-  if (sampled && !logits) return MTP_ERR_NULL;
+  const bool exact = sampled && smp->accept_rule == MTP_ACCEPT_EXACT;
+  if (sampled && !exact && !logits) return MTP_ERR_NULL;
+  if (exact && !smp->positions) return MTP_ERR_NULL;
   if (!aligned16(hidden) || !aligned16(row_stats) || (logits && !aligned16(logits))) return MTP_ERR_ALIGN;
+  if (exact && !aligned16(smp->positions)) return MTP_ERR_ALIGN;
   if ((wide ? lmhead_wide_lds_bytes() : lmhead_lds_bytes_for(head->wtype, head->d, M)) > kMaxLds) return MTP_ERR_SHAPE;
   if (!ws || !aligned256(ws)) return ws ? MTP_ERR_ALIGN : MTP_ERR_WORKSPACE;
   if (ws_bytes < lmhead_ws_bytes(M, head->vocab)) return MTP_ERR_WORKSPACE;
@@ -199,6 +208,7 @@ int mtp_verify_logits(const mtp_head* head, const void* hidden, int32_t htype, i
   p.key1 = (uint32_t)(smp->seed >> 32);
   p.cycle = smp->cycle;
   p.request_base = smp->request_base;
+  p.positions = exact ? smp->positions : nullptr;
   p.inv_t = inv_t_eff(smp->temperature);
   p.sampled = sampled;
   p.verify = 1;
@@ -230,10 +240,10 @@ int mtp_accept_sample(int32_t B, int32_t k, int32_t k_max, int32_t vocab, int32_
   if (vocab < 1 || n_draft < 1 || n_draft > vocab) return MTP_ERR_SHAPE;
   if (!draft_tokens || !draft_stats || !row_stats || !out_tokens || !n_accept || !n_emit || !flags)
     return MTP_ERR_NULL;
-  const bool sampled = smp->temperature > 0.0f;
-  if (sampled && (!draft_logits || !logits)) return MTP_ERR_NULL;
+  const bool ratio = ratio_sampling(smp);
+  if (ratio && (!draft_logits || !logits)) return MTP_ERR_NULL;
   if (!aligned16(draft_stats) || !aligned16(row_stats)) return MTP_ERR_ALIGN;
-  const size_t need = accept_ws_bytes(B, vocab, smp->temperature);
+  const size_t need = accept_ws_bytes(B, vocab, ratio);
   if (need > 0) {
     if (!ws) return MTP_ERR_WORKSPACE;
     if (!aligned256(ws)) return MTP_ERR_ALIGN;
@@ -246,6 +256,7 @@ int mtp_accept_sample(int32_t B, int32_t k, int32_t k_max, int32_t vocab, int32_
   p.vocab = vocab;
   p.n_draft = n_draft;
   p.temperature = smp->temperature;
+  p.exact = smp->accept_rule == MTP_ACCEPT_EXACT;
   p.eos = smp->eos_id;
   p.key0 = (uint32_t)(smp->seed & 0xFFFFFFFFu);
   p.key1 = (uint32_t)(smp->seed >> 32);

@@ -22,6 +22,7 @@ constexpr int kNoIndex = 0x7fffffff;
 constexpr uint32_t kStreamDraft = 0;
 constexpr uint32_t kStreamAccept = 1;
 constexpr uint32_t kStreamResample = 2;
+constexpr uint32_t kStreamTrunk = 3;   // the trunk's own sample, keyed by position
 
 // ---------------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32->64

@@ -19,7 +19,7 @@ constexpr int kLmheadMaxRows = 16;        // hidden rows per launch of the LM-he
 constexpr int kLmheadMaxWideRows = 128;   // hidden rows per launch of the wide verify kernel
 constexpr size_t kPartialBytes = 48;      // sizeof(RowAcc)
 constexpr int kAcceptThreads = 256;
-int accept_slices(int vocab, float temperature);
+int accept_slices(int vocab, bool residual);   // vocabulary slices of the residual draw
 
 struct LmheadLaunch {
   int wtype;
@@ -35,6 +35,8 @@ struct LmheadLaunch {
   int row_base;           // Philox row of hidden row 0 of a request (draft slot, or 0)
   int stream_id;          // Philox stream (0 draft, 2 verify)
   uint32_t key0, key1, cycle, request_base;
+  const int32_t* positions;   // verify with exact-match acceptance at T > 0: [B] position of
+                              // row 0; the sample then comes from the position-keyed stream 3
   float inv_t;            // 1 / T_eff
   int sampled;            // T > 0
   int verify;             // 1: verify pass, 0: draft head
@@ -62,6 +64,7 @@ hipError_t launch_lmhead_wide(const LmheadLaunch& p, hipStream_t stream);
 struct AcceptLaunch {
   int B, k, k_max, vocab, n_draft;
   float temperature;
+  int exact;              // T > 0: exact-match acceptance against the verify row's sample
   int eos;
   uint32_t key0, key1, cycle, request_base;
   const int32_t* drafts;
@@ -76,7 +79,7 @@ struct AcceptLaunch {
   void* ws;
 };
 
-size_t accept_ws_bytes(int B, int vocab, float temperature);
+size_t accept_ws_bytes(int B, int vocab, bool residual);
 hipError_t launch_accept(const AcceptLaunch& p, hipStream_t stream);
 
 struct CommitLaunch {

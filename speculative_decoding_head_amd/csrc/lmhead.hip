@@ -246,15 +246,19 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
 
   // ---- per-lane hidden rows: j = 4g + r -----------------------------------------
   int tok[4];
-  uint32_t prow[4], preq[4];
+  uint32_t prow[4], preq[4], pcyc[4];
   bool rvalid[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int j = 4 * g + r;
     rvalid[r] = j < M;
     const int b = j / p.rows_per_req, i = j % p.rows_per_req;
-    prow[r] = (uint32_t)(p.stream_id << 8) | (uint32_t)(i + p.row_base);
+    // counter words 1 and 3 of the row's draws: (stream, row) and the cycle, or for the
+    // trunk's own sample under exact-match acceptance (stream 3) the absolute position
+    const bool bypos = VERIFY && p.positions != nullptr;
+    prow[r] = bypos ? (uint32_t)(kStreamTrunk << 8) : (uint32_t)(p.stream_id << 8) | (uint32_t)(i + p.row_base);
     preq[r] = p.request_base + (uint32_t)b;
+    pcyc[r] = (bypos && rvalid[r]) ? (uint32_t)(p.positions[b] + i) : p.cycle;
     tok[r] = (VERIFY && rvalid[r] && i < p.k) ? p.drafts[(size_t)b * p.k_max + i] : -1;
   }
 
@@ -290,7 +294,7 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
         const float z = c[t][r];
         float gn = 0.0f;
         if (SAMPLED) {
-          const u32x4 wd = philox4x32_10(u32x4{(uint32_t)x >> 2, prow[r], preq[r], p.cycle}, p.key0, p.key1);
+          const u32x4 wd = philox4x32_10(u32x4{(uint32_t)x >> 2, prow[r], preq[r], pcyc[r]}, p.key0, p.key1);
           const int sel = x & 3;
           gn = gumbel_from_word(sel == 0 ? wd.x : (sel == 1 ? wd.y : (sel == 2 ? wd.z : wd.w)));
         }

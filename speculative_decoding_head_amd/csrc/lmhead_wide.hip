@@ -59,7 +59,8 @@ constexpr int kOffHbuf = kOffHtab + 2 * WU * kRows * 4;
 constexpr int kOffTok = kOffHbuf + 2 * kFragsPerChunk * 16;
 constexpr int kOffRow = kOffTok + kRows * 4;
 constexpr int kOffReq = kOffRow + kRows * 4;
-constexpr int kOffRun = kOffReq + kRows * 4;
+constexpr int kOffCyc = kOffReq + kRows * 4;
+constexpr int kOffRun = kOffCyc + kRows * 4;
 constexpr int kOffGum = kOffRun + kWaves * kRows * (int)sizeof(RowAcc);
 constexpr int kLdsBytes = kOffGum + kWaves * 4 * 16 * 16 * 4;
 
@@ -139,6 +140,7 @@ __device__ __forceinline__ void wide_body(const LmheadLaunch& p) {
   int* ltok = reinterpret_cast<int*>(smem + kOffTok);            // [128] drafted id per row
   uint32_t* lrow = reinterpret_cast<uint32_t*>(smem + kOffRow);  // [128] Philox row word
   uint32_t* lreq = reinterpret_cast<uint32_t*>(smem + kOffReq);  // [128] Philox request word
+  uint32_t* lcyc = reinterpret_cast<uint32_t*>(smem + kOffCyc);  // [128] Philox cycle / position word
   RowAcc* lrun = reinterpret_cast<RowAcc*>(smem + kOffRun);      // [8 waves][128] running state
   float* gum = reinterpret_cast<float*>(smem + kOffGum) + wave * 1024;   // this wave's [4 g][16 n][16 xi] noise
 
@@ -170,8 +172,11 @@ __device__ __forceinline__ void wide_body(const LmheadLaunch& p) {
   if (tid < kRows) {
     const int b = tid / p.rows_per_req, i = tid % p.rows_per_req;
     ltok[tid] = (tid < M && i < p.k) ? p.drafts[(size_t)b * p.k_max + i] : -1;
-    lrow[tid] = (uint32_t)(p.stream_id << 8) | (uint32_t)(i + p.row_base);
+    // exact-match acceptance at T > 0: the trunk's own sample, stream 3 keyed by position
+    const bool bypos = p.positions != nullptr;
+    lrow[tid] = bypos ? (uint32_t)(kStreamTrunk << 8) : (uint32_t)(p.stream_id << 8) | (uint32_t)(i + p.row_base);
     lreq[tid] = p.request_base + (uint32_t)b;
+    lcyc[tid] = (bypos && tid < M) ? (uint32_t)(p.positions[b] + i) : p.cycle;
   }
   for (int e = tid; e < kWaves * kRows; e += kLmheadThreads) rowacc_init(lrun[e]);
 
@@ -448,7 +453,7 @@ __device__ __forceinline__ void wide_body(const LmheadLaunch& p) {
           for (int t = 0; t < WTV; ++t) {
             if (!tval[t]) continue;
             // one Philox block = the Gumbel noise of these four ids
-            const u32x4 wd = philox4x32_10(u32x4{(uint32_t)x4[t] >> 2, lrow[j], lreq[j], p.cycle}, p.key0, p.key1);
+            const u32x4 wd = philox4x32_10(u32x4{(uint32_t)x4[t] >> 2, lrow[j], lreq[j], lcyc[j]}, p.key0, p.key1);
             const float gn[4] = {gumbel_from_word(wd.x), gumbel_from_word(wd.y), gumbel_from_word(wd.z),
                                  gumbel_from_word(wd.w)};
 #pragma unroll
@@ -475,7 +480,7 @@ __device__ __forceinline__ void wide_body(const LmheadLaunch& p) {
           if (!tval[t]) continue;
           const f32x4 zz = c[t][cb];
           u32x4 wd = u32x4{0u, 0u, 0u, 0u};
-          if (SAMPLED) wd = philox4x32_10(u32x4{(uint32_t)x4[t] >> 2, lrow[j], lreq[j], p.cycle}, p.key0, p.key1);
+          if (SAMPLED) wd = philox4x32_10(u32x4{(uint32_t)x4[t] >> 2, lrow[j], lreq[j], lcyc[j]}, p.key0, p.key1);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int x = x4[t] + r;
@@ -582,7 +587,7 @@ __device__ __forceinline__ void wide_body(const LmheadLaunch& p) {
 #pragma unroll 1
       for (int q = 0; q < 4; ++q) {
         const int j = (4 * h + a) * 16 + 4 * g + q;
-        const u32x4 wd = philox4x32_10(u32x4{(uint32_t)(4 * tile + m), lrow[j], lreq[j], p.cycle}, p.key0, p.key1);
+        const u32x4 wd = philox4x32_10(u32x4{(uint32_t)(4 * tile + m), lrow[j], lreq[j], lcyc[j]}, p.key0, p.key1);
         const f32x4 gv = f32x4{gumbel_from_word(wd.x), gumbel_from_word(wd.y), gumbel_from_word(wd.z),
                                gumbel_from_word(wd.w)};
         *reinterpret_cast<f32x4*>(gum + (16 * g + 4 * a + q) * 16 + 4 * m) = gv;

@@ -27,6 +27,7 @@ ROW_NONFINITE, ROW_POSINF, ROW_INVALID = 0x1, 0x2, 0x4
 ACC_ALL_ACCEPTED, ACC_EOS, ACC_RESID_FALLBACK, ACC_ROW_INVALID = 0x01, 0x02, 0x04, 0x08
 ACC_NONFINITE_TARGET, ACC_NONFINITE_DRAFT, ACC_DRAFT_INVALID = 0x10, 0x20, 0x40
 ROW_STATS_WORDS = 8   # sizeof(mtp_row_stats) / 4
+ACCEPT_RATIO, ACCEPT_EXACT = 0, 1
 
 EXPORTED = ("mtp_draft_head", "mtp_verify_logits", "mtp_accept_sample", "mtp_commit_state",
             "mtp_workspace_bytes", "mtp_tiled_bytes", "mtp_pack_head", "mtp_status_str", "mtp_abi_version")
@@ -44,7 +45,8 @@ class _Head(ctypes.Structure):
 
 class _Sampling(ctypes.Structure):
     _fields_ = [("temperature", ctypes.c_float), ("eos_id", ctypes.c_int32), ("seed", ctypes.c_uint64),
-                ("cycle", ctypes.c_uint32), ("request_base", ctypes.c_uint32)]
+                ("cycle", ctypes.c_uint32), ("request_base", ctypes.c_uint32), ("accept_rule", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("positions", ctypes.c_void_p)]
 
 
 _lib_handle = None
@@ -133,9 +135,13 @@ class Head:
 
 
 def sampling(temperature: float = 0.0, eos_id: int = -1, seed: int = 0, cycle: int = 0,
-             request_base: int = 0) -> _Sampling:
+             request_base: int = 0, accept_rule: int = ACCEPT_RATIO,
+             positions: Optional[torch.Tensor] = None) -> _Sampling:
+    """mtp_sampling.  ``positions`` (device int32 [B], for ACCEPT_EXACT at T > 0) must stay
+    alive until the stream has run the calls that use it."""
     return _Sampling(float(temperature), int(eos_id), int(seed) & (2**64 - 1), int(cycle) & 0xFFFFFFFF,
-                     int(request_base) & 0xFFFFFFFF)
+                     int(request_base) & 0xFFFFFFFF, int(accept_rule), 0,
+                     _ptr(positions, (torch.int32,), "positions"))
 
 
 def row_stats_empty(*shape, device="cuda") -> torch.Tensor:

@@ -44,8 +44,10 @@ class GpuCycle:
     """Device buffers for one cycle of B requests with k drafts."""
 
     def __init__(self, dhead: mtp.Head, n_draft: int, B: int, k: int, temperature: float, seed: int = 0,
-                 eos: int = -1, k_max: int | None = None):
+                 eos: int = -1, k_max: int | None = None, rule: int = mtp.ACCEPT_RATIO):
         self.h, self.n_draft, self.B, self.k = dhead, n_draft, B, k
+        self.rule = rule
+        self.positions = torch.zeros(B, dtype=torch.int32, device="cuda")
         self.k_max = k if k_max is None else k_max
         self.T, self.seed, self.eos = temperature, seed, eos
         V = dhead.vocab
@@ -65,8 +67,12 @@ class GpuCycle:
                  mtp.workspace_bytes(mtp.OP_ACCEPT, 0, V, B))
         self.ws = mtp.workspace(nb)
 
+    def set_positions(self, positions) -> None:
+        """Absolute position verify row 0 of each request predicts (exact-match rule)."""
+        self.positions.copy_(torch.as_tensor(np.asarray(positions, dtype=np.int32)))
+
     def smp(self, cycle=0, request_base=0):
-        return mtp.sampling(self.T, self.eos, self.seed, cycle, request_base)
+        return mtp.sampling(self.T, self.eos, self.seed, cycle, request_base, self.rule, self.positions)
 
     def draft(self, slot: int, h_slot: torch.Tensor, cycle=0, request_base=0):
         mtp.mtp_draft_head(self.h, self.n_draft, h_slot, slot, self.k_max, self.smp(cycle, request_base),

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mtp_abi_version() == 1
+    assert lib.mtp_abi_version() == 2
     for code in range(-7, 1):
         s = lib.mtp_status_str(code)
         assert s and s != b"unknown status"
@@ -130,6 +130,30 @@ def test_verify_rejects_bad_arguments(lib, case, want):
     r = lib.mtp_verify_logits(ctypes.byref(head), FAKE, mtp.H_BF16, a["B"], a["k"], a["drafts"], a["k_max"],
                               ctypes.byref(smp), a["stats"], None, FAKE, a["ws_bytes"], None)
     assert r == want
+
+
+@pytest.mark.parametrize("fields,want", [
+    (dict(accept_rule=2), -4),                                   # no such rule
+    (dict(accept_rule=-1), -4),
+    (dict(reserved=1), -4),
+    (dict(accept_rule=1, positions=None), -1),                   # exact rule at T > 0 needs positions
+    (dict(accept_rule=1, positions=FAKE + 4), -5),
+])
+def test_verify_rejects_bad_sampling(lib, fields, want):
+    f = dict(temperature=1.0, eos_id=-1, seed=0, cycle=0, request_base=0, accept_rule=0, reserved=0, positions=FAKE)
+    f.update(fields)
+    smp = mtp.mtp._Sampling(**f)
+    head = _head()
+    r = lib.mtp_verify_logits(ctypes.byref(head), FAKE, mtp.H_BF16, 1, 3, FAKE, 3, ctypes.byref(smp), FAKE, FAKE,
+                              FAKE, 1 << 24, None)
+    assert r == want
+
+
+def test_sampling_struct_layout():
+    # mirrors mtp_sampling: float, int32, uint64, uint32, uint32, int32, int32, pointer
+    S = mtp.mtp._Sampling
+    assert ctypes.sizeof(S) == 40
+    assert [S.seed.offset, S.cycle.offset, S.accept_rule.offset, S.positions.offset] == [8, 16, 24, 32]
 
 
 @pytest.mark.parametrize("case,want", [

@@ -103,3 +103,23 @@ def test_gumbel_max_samples_the_softmax():
     u = O.uniform_gumbel(O.philox_words(5, 2, 0, np.arange(n)[:, None], 0, np.arange(logits.size)))
     bad = O.argmax_lowest_f32(logits[None, :] + np.log(u))
     assert stats.chisquare(np.bincount(bad, minlength=logits.size), n * np.exp(logits)).pvalue < 1e-6
+
+
+def test_trunk_draw_is_keyed_by_position_and_samples_the_softmax():
+    # the trunk's own draw (stream 3): one word per (request, position); over positions it
+    # samples softmax(z/T) (Gumbel-max), and it does not depend on anything but the position
+    T = 0.8
+    z = np.array([1.0, 0.4, 0.0, -0.3, -2.0])
+    n = 30000
+    picks = np.array([O.trunk_sample(z, T, 77, 3, pos)[0] for pos in range(n)])
+    p = np.exp(z / T) / np.exp(z / T).sum()
+    assert stats.chisquare(np.bincount(picks, minlength=z.size), n * p).pvalue > 1e-4
+    # counter layout (x >> 2, 3 << 8, request, position)
+    w = O.philox_words(77, 3, 0, 3, 1234, np.arange(z.size))
+    u = O.uniform_gumbel(w)
+    assert np.array_equal(O.trunk_noise(77, 3, 1234, z.size), -np.log(-np.log(u)))
+    assert O.trunk_sample(z, T, 77, 3, 1234)[0] == int(O.argmax_lowest_f32(z / T - np.log(-np.log(u))))
+    # another request or position gives other draws; the draft and resample streams differ
+    assert not np.array_equal(O.trunk_noise(77, 3, 1234, 8), O.trunk_noise(77, 4, 1234, 8))
+    assert not np.array_equal(O.trunk_noise(77, 3, 1234, 8), O.trunk_noise(77, 3, 1235, 8))
+    assert not np.array_equal(O.trunk_noise(77, 3, 1234, 8), O.gumbel_noise(77, O.STREAM_RESAMPLE, 0, 3, 1234, 8))

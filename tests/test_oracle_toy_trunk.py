@@ -1,7 +1,9 @@
 """End-to-end pins of the oracle on a tiny recurrent trunk.
 
 Greedy speculative decoding must emit exactly the tokens of ordinary argmax decoding
-(lucebox-hub PR "feat(qwen4exp): MTP speculative decoding", section "Exactness"), and
+(lucebox-hub PR "feat(qwen4exp): MTP speculative decoding", section "Exactness"), so must
+sampled decoding with exact-match acceptance against ordinary sampled decoding under the
+same seed (same PR, "Exactness" and "Notes"; the trunk's draws are keyed by position), and
 after every commit the live recurrent state, the KV rows and kv_len must equal those of
 ordinary decoding after the same number of tokens (DS4Server issue "Add Qwen3.8 Flash
 Next native MTP speculation", section "Completion requirements": rejected rows leave every
@@ -31,12 +33,30 @@ def ordinary_greedy(tt: ToyTrunk, t0: int, n: int):
     return out, states, kv
 
 
+def ordinary_sampled(tt: ToyTrunk, t0: int, n: int, T: float, seed: int):
+    """Decoding without speculation at temperature T: the token at position p is the
+    trunk's own draw at p."""
+    S = tt.zero_state()
+    t = t0
+    out, states, kv = [], [], []
+    for pos in range(n):
+        S = tt.step(S, t)
+        kv.append(tt.kv_row(t))
+        y, _ = O.trunk_sample(tt.W @ tt.hidden(S, t), T, seed, 0, pos)
+        out.append(y)
+        states.append(tt.state_bytes(S))
+        t = y
+    return out, states, kv
+
+
 def _kv_bytes(row: np.ndarray) -> np.ndarray:
     return np.frombuffer(row.tobytes(), dtype=np.uint8)
 
 
-def speculative_greedy(tt: ToyTrunk, t0: int, n: int, k: int, n_draft: int, forced=None):
-    """Drive draft -> verify -> accept -> commit with the oracle; yield per-cycle snapshots."""
+def speculative_greedy(tt: ToyTrunk, t0: int, n: int, k: int, n_draft: int, forced=None,
+                       T: float = 0.0, seed: int = 0):
+    """Drive draft -> verify -> accept -> commit with the oracle; yield per-cycle snapshots.
+    T > 0: exact-match acceptance against the trunk's position-keyed draws."""
     W = tt.W
     S = tt.zero_state()
     row_bytes = tt.kv_dim * 8
@@ -74,8 +94,15 @@ def speculative_greedy(tt: ToyTrunk, t0: int, n: int, k: int, n_draft: int, forc
             r = _kv_bytes(tt.kv_row(tk))
             kv[0, 0, 0, kv_len[0] + i] = r
             kv[0, 0, 1, kv_len[0] + i] = r[::-1]
-        zv = (np.array(hv) @ W.T)[None]
-        acc = O.accept(np.array([drafts]), None, zv, n_draft, 0.0, 0, c, -1, 1e-9)
+        if T > 0:
+            # verify row 0 predicts the token at position len(emitted)
+            vr = O.verify_rows(W, np.array(hv)[None], np.array([drafts]), T, seed, c, 1e-9,
+                               positions=[len(emitted)])
+            acc = O.accept(np.array([drafts]), None, vr["logits"], n_draft, T, seed, c, -1, 1e-9,
+                           rule=O.RULE_EXACT, target=vr)
+        else:
+            zv = (np.array(hv) @ W.T)[None]
+            acc = O.accept(np.array([drafts]), None, zv, n_draft, 0.0, 0, c, -1, 1e-9)
         live, kv, kv_len = O.commit(np.array([snaps]), np.zeros((1, snaps[0].size), np.uint8), kv, kv_len,
                                     acc["n_accept"], k)
         S = np.frombuffer(live[0].tobytes(), dtype=np.float64).reshape(S.shape).copy()
@@ -200,3 +227,36 @@ def test_planted_wrong_row_in_exact_match_is_caught(monkeypatch):
     want, _, _ = ordinary_greedy(tt, 0, 100)
     got, _ = speculative_greedy(tt, 0, 100, 3, n_draft=tt.V)
     assert got != want[:100]
+
+
+@pytest.mark.parametrize("k", [1, 3, 7])
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("T", [0.7, 1.0])
+def test_exact_match_sampling_equals_ordinary_sampling(k, seed, T):
+    tt = ToyTrunk(seed)
+    n = 150
+    want, states, kv_rows = ordinary_sampled(tt, 0, n + 8, T, 1234 + seed)
+    got, cycles = speculative_greedy(tt, 0, n, k, n_draft=tt.V, T=T, seed=1234 + seed)
+    assert got == want[:n]
+    _check_state(tt, cycles, states, kv_rows)
+    # sampling departs from the argmax path, and drafts are both kept and rejected
+    assert got != ordinary_greedy(tt, 0, n)[0]
+    assert len({cy["n_accept"] for cy in cycles}) >= 2
+
+
+def test_planted_cycle_keyed_trunk_draw_is_caught(monkeypatch):
+    # the trunk's draw keyed by (cycle, row) instead of position: no longer the output
+    # of ordinary sampling
+    calls = {"n": 0}
+    real = O.trunk_noise
+
+    def by_call(seed, b, position, n):
+        calls["n"] += 1
+        return real(seed, b, position + 7 * calls["n"], n)
+    monkeypatch.setattr(O, "trunk_noise", by_call)
+    tt = ToyTrunk(2)
+    got, _ = speculative_greedy(tt, 0, 60, 3, n_draft=tt.V, T=1.0, seed=5)
+    calls["n"] = 0
+    monkeypatch.setattr(O, "trunk_noise", real)
+    want, _, _ = ordinary_sampled(tt, 0, 60, 1.0, 5)
+    assert got != want
