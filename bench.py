@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="model_greedy", choices=["model_greedy", "q4_greedy", "q4_sampled", "batched_commit"])
+    ap.add_argument("--workload", default="model_greedy", choices=["model_greedy", "q4_greedy", "q4_sampled", "exact_sampled", "batched_commit"])
     ap.add_argument("--cpu-cycles", type=int, default=0, help="oracle cycles for the CPU baseline (0 = auto)")
     ap.add_argument("--event-every", type=int, default=10,
                     help="record per-kernel HIP events in every N-th timed cycle (each event is a queue packet "
@@ -176,13 +176,16 @@ def main():
         dh = mtp.tiled_head(dh)
         torch.cuda.synchronize()
     B, k, nd, V, d, T = wl.B, wl.k, wl.n_draft, wl.V, wl.d, wl.temperature
+    exact = T > 0 and wl.accept_rule == "exact"
+    rule = mtp.ACCEPT_EXACT if exact else mtp.ACCEPT_RATIO
     hv_t = torch.from_numpy(hv.view(np.int16)).to(dev)                          # [B][k+1][d]
     hd_slots = [torch.from_numpy(np.ascontiguousarray(hd[:, i]).view(np.int16)).to(dev) for i in range(k)]
     dtok = torch.zeros(B, k, dtype=torch.int32, device=dev)
     dst = mtp.row_stats_empty(B, k)
-    dlg = torch.zeros(B, k, nd, dtype=torch.float32, device=dev) if T > 0 else None
+    # exact-match acceptance reads neither the draft logits nor the verify logits
+    dlg = torch.zeros(B, k, nd, dtype=torch.float32, device=dev) if T > 0 and not exact else None
     vst = mtp.row_stats_empty(B, k + 1)
-    vlg = torch.zeros(B, k + 1, V, dtype=torch.float32, device=dev) if T > 0 else None
+    vlg = torch.zeros(B, k + 1, V, dtype=torch.float32, device=dev) if T > 0 and not exact else None
     out = torch.zeros(B, k + 1, dtype=torch.int32, device=dev)
     nacc = torch.zeros(B, dtype=torch.int32, device=dev)
     nemit = torch.zeros(B, dtype=torch.int32, device=dev)
@@ -201,13 +204,15 @@ def main():
         kv_rows = KV_ROWS + (k + 1) * (args.warmup + args.steps + 16 + args.extra_cycles)
         kv = torch.zeros(B, KV_LAYERS, 2, kv_rows, kv_row_bytes, dtype=torch.uint8, device=dev)
         kv_len = torch.zeros(B, dtype=torch.int32, device=dev)
+    # the position verify row 0 predicts: the committed length (exact-match rule)
+    positions = kv_len if with_commit else torch.zeros(B, dtype=torch.int32, device=dev)
     setup_s = time.time() - t0
 
     stream = torch.cuda.current_stream()
 
     def cycle(c, events=None, hidden=None):
         hv_c, hd_c = (hv_t, hd_slots) if hidden is None else hidden
-        smp = mtp.sampling(T, wl.eos, wl.philox_seed, c, 0)
+        smp = mtp.sampling(T, wl.eos, wl.philox_seed, c, 0, rule, positions if exact else None)
         if events is not None:
             events[0].record(stream)
         for i in range(k):
@@ -263,8 +268,8 @@ def main():
     # algorithmic bytes per launch (weights read once, hidden rows, outputs)
     wrow = {"bf16": d * 2, "q4a32": d // 2 + 2 * 2 * (d // 32)}[wl.wtype]
     hbytes = d * 2
-    draft_bytes = nd * wrow + B * hbytes + B * (32 + 4) + (B * nd * 4 if T > 0 else 0)
-    verify_bytes = V * wrow + B * (k + 1) * hbytes + B * (k + 1) * 32 + (B * (k + 1) * V * 4 if T > 0 else 0)
+    draft_bytes = nd * wrow + B * hbytes + B * (32 + 4) + (B * nd * 4 if dlg is not None else 0)
+    verify_bytes = V * wrow + B * (k + 1) * hbytes + B * (k + 1) * 32 + (B * (k + 1) * V * 4 if vlg is not None else 0)
     commit_bytes = (2 * B * state_bytes) if with_commit else 0
     cycle_bytes = k * draft_bytes + verify_bytes + commit_bytes
     d_avg = float(np.mean(draft_ms)) * 1e-3
@@ -304,7 +309,8 @@ def main():
         "dtype": "bf16" if wl.wtype == "bf16" else "q4a32",
         "data": "synthetic",
         "config": {"workload": args.workload, "d": d, "V": V, "n_draft": nd, "k": k, "batch": B,
-                   "temperature": T, "weights": wl.wtype, "layout": "row-major" if args.row_major else "tiled",
+                   "temperature": T, "accept_rule": wl.accept_rule if T > 0 else "exact (greedy)",
+                   "weights": wl.wtype, "layout": "row-major" if args.row_major else "tiled",
                    "accumulate": "fp32",
                    "step": f"{k} draft-head calls + verify ({B * (k + 1)} rows) + accept"
                            + (" + commit (36 MiB snapshot select, 12-layer KV trim)" if with_commit else "")},
@@ -326,7 +332,7 @@ def main():
                                   None if dh.scale is None else dh.scale.clone(),
                                   None if dh.minv is None else dh.minv.clone())
                          for _ in range(args.rotate_heads - 1)]
-        smp = mtp.sampling(T, wl.eos, wl.philox_seed, 0, 0)
+        smp = mtp.sampling(T, wl.eos, wl.philox_seed, 0, 0, rule, positions if exact else None)
         n = args.extra_cycles * k
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
         for j in range(len(copies)):
@@ -414,7 +420,8 @@ def cpu_baseline(wl, head, hv, hd, n_cycles, with_commit, state_bytes):
     done = 0
     t0 = time.perf_counter()
     while True:
-        o = O.cycle(W, wl.n_draft, hd64, hv64, wl.temperature, wl.philox_seed, done, wl.eos, delta)
+        o = O.cycle(W, wl.n_draft, hd64, hv64, wl.temperature, wl.philox_seed, done, wl.eos, delta,
+                    rule=wl.accept_rule, positions=np.full(wl.B, done * (wl.k + 1)))
         if with_commit:
             O.commit(snaps, live, kv, kv_len, o["accept"]["n_accept"], wl.k)
         done += 1

@@ -160,6 +160,7 @@ class Workload:
     philox_seed: int     # key of the counter-based generator
     eos: int = -1
     sigma: float = 0.02
+    accept_rule: str = "ratio"   # at T > 0: "ratio" (u q <= p) or "exact" (draft == the trunk's draw)
     # recurrent state / KV (commit); zero means no state in this workload
     n_state_layers: int = 0
     state_heads: int = 0
@@ -194,6 +195,11 @@ WORKLOADS: Dict[str, Workload] = {
                           wtype=WT_Q4A32, htype=HT_BF16, temperature=0.0, seed=0, philox_seed=1234),
     "q4_sampled": Workload("q4_sampled", d=2560, V=152064, n_draft=64000, k=7, B=1,
                            wtype=WT_Q4A32, htype=HT_BF16, temperature=1.0, seed=0, philox_seed=1234),
+    # sampled verify at model scale with exact-match acceptance (the trunk's draws keyed
+    # by position): argmax drafts, no draft logits, no residual
+    "exact_sampled": Workload("exact_sampled", d=2560, V=152064, n_draft=64000, k=7, B=1,
+                              wtype=WT_BF16, htype=HT_BF16, temperature=1.0, seed=0, philox_seed=1234,
+                              accept_rule="exact"),
     # 16 requests x 8 verify rows, per-request acceptance, commit of 36-layer fp32 state
     "batched_commit": Workload("batched_commit", d=2560, V=152064, n_draft=64000, k=7, B=16,
                                wtype=WT_BF16, htype=HT_BF16, temperature=0.0, seed=0, philox_seed=0,
