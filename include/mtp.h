@@ -269,6 +269,49 @@ int mtp_commit_state(int32_t B, int32_t k, const int32_t* n_accept, const void* 
                      int32_t max_rows, size_t kv_row_bytes, int32_t* kv_len, void* stream);
 
 /* ---------------------------------------------------------------------------------- */
+/* adaptive verify width (host side)                                                   */
+/* ---------------------------------------------------------------------------------- */
+/* lucebox-hub PR above, section "What": by default the verify width adapts, up to seven
+ * drafts, from the acceptance seen at each draft depth and a per-request fit of the
+ * cycle's cost.  One controller per request stream, owned by the caller; host memory
+ * only, no device work.  The metrics the PR reports (drafted and accepted tokens,
+ * verifier passes, acceptance depths) are its counters.
+ *   alpha[j]  exponential moving average (weight `decay` per observation) of "draft j+1
+ *             was accepted", over cycles that reached draft j+1; a block that ended with
+ *             EOS or at an unusable target row leaves its stopping depth untouched;
+ *   E(k)      = 1 + sum_{i=1..k} prod_{j<i} alpha[j]   (expected tokens of a k-draft cycle);
+ *   c(k)      = c0 + c1 k, least squares over the observed (k, seconds) pairs with weights
+ *             decaying by (1 - decay) per observation; fewer than two distinct widths:
+ *             c1 = slope_prior * c0; a negative fitted slope is taken as 0; no timing
+ *             yet: c0 = 1, c1 = slope_prior;
+ *   choose    = argmax over 1 <= k <= k_max of E(k) / c(k) (smallest k on ties; widths
+ *             priced at <= 0 are skipped; 1 if all are). */
+typedef struct mtp_width_ctl {
+  int32_t k_max;                 /* 1..7                                                  */
+  int32_t reserved;
+  double decay;                  /* (0, 1]                                                */
+  double slope_prior;            /* >= 0: c1 / c0 until two widths have been timed         */
+  double alpha[7];
+  double sw, sk, skk, st, skt;   /* decayed sums of 1, k, k^2, t, k t                       */
+  uint64_t verifier_passes;      /* mtp_width_observe calls                                */
+  uint64_t cycles;               /* request-cycles observed                                */
+  uint64_t drafted, accepted;    /* drafts made / drafts kept                              */
+  uint64_t depth_hist[8];        /* request-cycles that kept a = 0..7 drafts               */
+} mtp_width_ctl;
+
+/* alpha[*] = alpha0 in [0, 1]; counters and sums zero.  MTP_ERR_RANGE / _SHAPE on bad
+ * arguments. */
+int mtp_width_init(mtp_width_ctl* c, int32_t k_max, double decay, double alpha0, double slope_prior);
+/* One verify pass of B requests with k drafts each: n_accept and flags are HOST copies
+ * of mtp_accept_sample's outputs; seconds = the pass's measured cycle time (<= 0: not
+ * timed).  MTP_ERR_RANGE if some n_accept is outside [0, k]; nothing is updated then. */
+int mtp_width_observe(mtp_width_ctl* c, int32_t k, int32_t B, const int32_t* n_accept, const uint32_t* flags,
+                      double seconds);
+double mtp_width_expected_tokens(const mtp_width_ctl* c, int32_t k);   /* E(k), 0 <= k <= 7   */
+double mtp_width_cost(const mtp_width_ctl* c, int32_t k);              /* c(k)                */
+int32_t mtp_width_choose(const mtp_width_ctl* c);                      /* k*, in 1..k_max     */
+
+/* ---------------------------------------------------------------------------------- */
 /* weight preparation                                                                  */
 /* ---------------------------------------------------------------------------------- */
 /* Bytes of one array of a tiled head for a source of type wtype (MTP_W_BF16 or

@@ -30,11 +30,21 @@ ROW_STATS_WORDS = 8   # sizeof(mtp_row_stats) / 4
 ACCEPT_RATIO, ACCEPT_EXACT = 0, 1
 
 EXPORTED = ("mtp_draft_head", "mtp_verify_logits", "mtp_accept_sample", "mtp_commit_state",
-            "mtp_workspace_bytes", "mtp_tiled_bytes", "mtp_pack_head", "mtp_status_str", "mtp_abi_version")
+            "mtp_workspace_bytes", "mtp_tiled_bytes", "mtp_pack_head", "mtp_status_str", "mtp_abi_version",
+            "mtp_width_init", "mtp_width_observe", "mtp_width_expected_tokens", "mtp_width_cost",
+            "mtp_width_choose")
 
 
 class MtpError(RuntimeError):
     pass
+
+
+class _WidthCtl(ctypes.Structure):
+    _fields_ = [("k_max", ctypes.c_int32), ("reserved", ctypes.c_int32), ("decay", ctypes.c_double),
+                ("slope_prior", ctypes.c_double), ("alpha", ctypes.c_double * 7), ("sw", ctypes.c_double),
+                ("sk", ctypes.c_double), ("skk", ctypes.c_double), ("st", ctypes.c_double), ("skt", ctypes.c_double),
+                ("verifier_passes", ctypes.c_uint64), ("cycles", ctypes.c_uint64), ("drafted", ctypes.c_uint64),
+                ("accepted", ctypes.c_uint64), ("depth_hist", ctypes.c_uint64 * 8)]
 
 
 class _Head(ctypes.Structure):
@@ -77,6 +87,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mtp_status_str.argtypes = [ctypes.c_int]
     lib.mtp_status_str.restype = ctypes.c_char_p
     lib.mtp_abi_version.argtypes = []
+    wp, f64 = ctypes.POINTER(_WidthCtl), ctypes.c_double
+    lib.mtp_width_init.argtypes = [wp, i32, f64, f64, f64]
+    lib.mtp_width_init.restype = ctypes.c_int
+    lib.mtp_width_observe.argtypes = [wp, i32, i32, vp, vp, f64]
+    lib.mtp_width_observe.restype = ctypes.c_int
+    for f in ("mtp_width_expected_tokens", "mtp_width_cost"):
+        getattr(lib, f).argtypes = [wp, i32]
+        getattr(lib, f).restype = f64
+    lib.mtp_width_choose.argtypes = [wp]
+    lib.mtp_width_choose.restype = i32
     _lib_handle = lib
     return lib
 
@@ -249,3 +269,43 @@ def mtp_commit_state(B: int, k: int, n_accept: torch.Tensor, snapshots: Optional
                                 _ptr(snapshots, name="snapshots"), _ptr(live, name="live"), int(state_bytes),
                                 _ptr(kv, name="kv"), int(n_layers), int(max_rows), int(kv_row_bytes),
                                 _ptr(kv_len, (torch.int32,), "kv_len"), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------------
+# adaptive verify width (host side; same names as the C ABI's mtp_width_*)
+# ---------------------------------------------------------------------------------
+class WidthController:
+    """One mtp_width_ctl: feed it each cycle's acceptance outputs and time, ask it for k."""
+
+    def __init__(self, k_max: int = 7, decay: float = 0.1, alpha0: float = 0.8, slope_prior: float = 0.1):
+        self._c = _WidthCtl()
+        _check(load_library().mtp_width_init(ctypes.byref(self._c), int(k_max), float(decay), float(alpha0),
+                                             float(slope_prior)))
+
+    def observe(self, k: int, n_accept, flags, seconds: float) -> None:
+        import numpy as np
+        a = np.ascontiguousarray(np.asarray(n_accept.cpu() if hasattr(n_accept, "cpu") else n_accept, dtype=np.int32))
+        f = np.ascontiguousarray(np.asarray(flags.cpu() if hasattr(flags, "cpu") else flags).astype(np.uint32))
+        if a.shape != f.shape or a.ndim != 1:
+            raise MtpError("n_accept and flags must be [B]")
+        _check(load_library().mtp_width_observe(ctypes.byref(self._c), int(k), int(a.size), a.ctypes.data,
+                                                f.ctypes.data, float(seconds)))
+
+    def expected_tokens(self, k: int) -> float:
+        return load_library().mtp_width_expected_tokens(ctypes.byref(self._c), int(k))
+
+    def cost(self, k: int) -> float:
+        return load_library().mtp_width_cost(ctypes.byref(self._c), int(k))
+
+    def choose(self) -> int:
+        return int(load_library().mtp_width_choose(ctypes.byref(self._c)))
+
+    @property
+    def alpha(self):
+        return list(self._c.alpha)
+
+    @property
+    def counters(self) -> dict:
+        c = self._c
+        return dict(verifier_passes=c.verifier_passes, cycles=c.cycles, drafted=c.drafted, accepted=c.accepted,
+                    depth_hist=list(c.depth_hist))
