@@ -103,6 +103,10 @@ typedef struct mtp_head {
   const void* w;       /* device, layout per wtype                                     */
   const void* scale;   /* device, Q4A32 only (else NULL)                               */
   const void* minv;    /* device, Q4A32 only (else NULL)                               */
+  const int32_t* row_ids; /* device int32 [vocab] or NULL: the vocabulary id of each row,
+                           * strictly ascending (a draft head gathered from a set of ids,
+                           * see mtp_gather_rows); NULL = row r is id r.  Only the draft
+                           * head takes a head with row ids.                          */
 } mtp_head;
 
 /* ---------------------------------------------------------------------------------- */
@@ -197,6 +201,10 @@ size_t mtp_workspace_bytes(int32_t op, int32_t rows, int32_t n_vocab_rows, int32
  *   T = 0: token = lowest-id argmax of z;  T > 0: token = argmax(z/T + Gumbel(stream 0,
  *   row = slot)), a sample of q = softmax(z/T) over the first n_draft ids.  Under
  *   MTP_ACCEPT_EXACT the draft head works as at T = 0 (argmax, statistics at T_eff = 1).
+ *   A head with row_ids (the same PR, "What": control/special tokens plus the lowest
+ *   ids) scores its n_draft rows and reports vocabulary ids: the token, the argmax and
+ *   the Gumbel draws (keyed by the vocabulary id) refer to row_ids[r]; draft_logits stay
+ *   indexed by row.
  * hidden:        [B][d] in htype.
  * draft_tokens:  int32 [B][k_max]; writes column `slot`; -1 for an all -inf row.
  * draft_stats:   mtp_row_stats [B][k_max]; writes column `slot`.
@@ -244,13 +252,15 @@ int mtp_verify_logits(const mtp_head* head, const void* hidden, int32_t htype, i
  *   all k accepted: a bonus token from row k (argmax, or the stream-2 sample).
  * Inputs are the outputs of the draft and verify calls of the same cycle (draft_logits
  * and logits are read only when T > 0 under MTP_ACCEPT_RATIO).  vocab and n_draft must
- * match those calls.
+ * match those calls.  draft_row_of: device int32 [vocab], the draft row of vocabulary id
+ * x or -1 (the inverse of the draft head's row_ids; q is 0 off its rows), or NULL when
+ * the draft rows are ids 0..n_draft-1; read only when T > 0 under MTP_ACCEPT_RATIO.
  * out_tokens: int32 [B][k+1] = d_1..d_a, last, then -1;  n_accept, n_emit: int32 [B]
  * (n_emit = n_accept + 1 except with MTP_ACC_ROW_INVALID);  flags: uint32 [B].        */
 int mtp_accept_sample(int32_t B, int32_t k, int32_t k_max, int32_t vocab, int32_t n_draft,
                       const mtp_sampling* smp, const int32_t* draft_tokens,
                       const mtp_row_stats* draft_stats, const float* draft_logits,
-                      const mtp_row_stats* row_stats, const float* logits,
+                      const mtp_row_stats* row_stats, const float* logits, const int32_t* draft_row_of,
                       int32_t* out_tokens, int32_t* n_accept, int32_t* n_emit, uint32_t* flags,
                       void* ws, size_t ws_bytes, void* stream);
 
@@ -318,6 +328,16 @@ int32_t mtp_width_choose(const mtp_width_ctl* c);                      /* k*, in
  * MTP_W_Q4A32): part 0 = w, 1 = scale, 2 = minv (0 for a part the format lacks, or for
  * invalid arguments). */
 size_t mtp_tiled_bytes(int32_t wtype, int32_t d, int32_t vocab, int32_t part);
+
+/* Gather rows of a row-major head (F32, BF16 or Q4A32) into a new row-major head, once,
+ * at load time: row r of dst = row ids[r] of src, with its scales and mins (lucebox-hub
+ * PR, "What": the draft head is a subset of the vocabulary).  ids: device int32 [n],
+ * strictly ascending ids in [0, src->vocab) (an id outside gives a zero row); dst_* hold
+ * n rows of src's formats (dst_scale and dst_minv for Q4A32 only), 16-byte aligned, not
+ * overlapping src.  The result is used with row_ids = ids, directly or after
+ * mtp_pack_head. */
+int mtp_gather_rows(const mtp_head* src, const int32_t* ids, int32_t n, void* dst_w, void* dst_scale,
+                    void* dst_minv, void* stream);
 
 /* Repack a row-major BF16 or Q4A32 head into the tiled layout (MTP_W_BF16_TILED /
  * MTP_W_Q4A32_TILED) on the device, once, at load time.  dst_* are device buffers of

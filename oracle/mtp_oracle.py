@@ -28,7 +28,9 @@ pages the method is described on, cited by title and section:
       trimmed [DS4-98 "Implementation"; MTP-PR "Exactness"; PORT-PR on-device checkpoints]
 
 Readings where the pages are silent (each is a stated choice, listed with the design):
-  * draft vocabulary = the first n_draft ids of the shared head;
+  * draft vocabulary = the first n_draft ids of the shared head, or a strictly ascending
+    id list (control/special tokens plus the lowest ids [MTP-PR "What"]); draws for a
+    draft row are keyed by its vocabulary id;
   * argmax ties go to the lowest id;
   * NaN -> -inf; a row holding +inf becomes uniform over its +inf ids; an all -inf
     target row stops the block before that row (flag ROW_INVALID, no correction token);
@@ -131,11 +133,13 @@ def uniform_gumbel(w) -> np.ndarray:
     return ((w >> np.uint64(9)) * np.uint64(2) + np.uint64(1)).astype(np.float64) * 2.0 ** -24
 
 
-def gumbel_noise(seed: int, stream: int, row, b, cycle: int, n: int) -> np.ndarray:
-    """Standard Gumbel noise -ln(-ln u) for ids 0..n-1; shape broadcast(b, row) + (n,)."""
+def gumbel_noise(seed: int, stream: int, row, b, cycle: int, n: int, ids=None) -> np.ndarray:
+    """Standard Gumbel noise -ln(-ln u) for ids 0..n-1 (or for the given ids); shape
+    broadcast(b, row) + (n,)."""
     b = np.asarray(b)[..., None]
     row = np.asarray(row)[..., None]
-    u = uniform_gumbel(philox_words(seed, stream, row, b, cycle, np.arange(n)))
+    xs = np.arange(n) if ids is None else np.asarray(ids)
+    u = uniform_gumbel(philox_words(seed, stream, row, b, cycle, xs))
     return -np.log(-np.log(u))
 
 
@@ -259,26 +263,30 @@ def _teff(T: float) -> float:
 # O1-O3  draft head
 # ----------------------------------------------------------------------------------
 def draft_rows(W64: np.ndarray, n_draft: int, h: np.ndarray, T: float, seed: int,
-               slot: int, cycle: int, delta: float, b_ids=None) -> dict:
+               slot: int, cycle: int, delta: float, b_ids=None, ids=None) -> dict:
     """One draft-head call for B requests (one hidden row each) [MTP-PR "What"].
 
-    The head is the first n_draft rows of the shared LM head.  T == 0: the draft is the
-    lowest-id argmax.  T > 0: the draft is argmax(z/T + Gumbel) over ids < n_draft, i.e.
-    a sample from q = softmax(z/T) restricted to the draft vocabulary.  Also returns the
-    row statistics (max, lse of z/T) and the raw logits, which the acceptance step needs.
+    The head is the first n_draft rows of the shared LM head, or its rows ``ids`` (the
+    draft vocabulary as an ascending id list, n_draft = len(ids)).  T == 0: the draft is
+    the lowest-id argmax.  T > 0: the draft is argmax(z/T + Gumbel) over the draft
+    vocabulary (noise keyed by the vocabulary id), i.e. a sample from q = softmax(z/T)
+    restricted to it.  Also returns the row statistics (max, lse of z/T) and the raw
+    logits (indexed by draft row), which the acceptance step needs.
     """
     B = h.shape[0]
     b_ids = np.arange(B) if b_ids is None else np.asarray(b_ids)
-    z = logits_f64(W64[:n_draft], h)
+    rows = np.arange(n_draft) if ids is None else np.asarray(ids, dtype=np.int64)
+    z = logits_f64(W64[rows], h)
     zs, rflags = sanitize(z)
     if T > 0:
-        G = gumbel_noise(seed, STREAM_DRAFT, slot, b_ids, cycle, n_draft)
-        token = argmax_lowest_f32(_f32_add(zs / T, G))
+        G = gumbel_noise(seed, STREAM_DRAFT, slot, b_ids, cycle, rows.size, ids=rows)
+        local = argmax_lowest_f32(_f32_add(zs / T, G))
         margin, thr = top2_gap(zs / T + G), delta / T
     else:
-        token = argmax_lowest_f32(zs)
+        local = argmax_lowest_f32(zs)
         margin, thr = top2_gap(zs), delta
-    z_tok = np.where(token >= 0, np.take_along_axis(zs, np.maximum(token, 0)[:, None], 1)[:, 0], NEG_INF)
+    token = np.where(local >= 0, rows[np.maximum(local, 0)], -1)
+    z_tok = np.where(local >= 0, np.take_along_axis(zs, np.maximum(local, 0)[:, None], 1)[:, 0], NEG_INF)
     return dict(token=token, max=zs.max(axis=-1), lse=logsumexp_rows(zs / _teff(T)), z_tok=z_tok,
                 flags=rflags, logits=z, margin=margin, near_tie=margin <= thr)
 
@@ -352,7 +360,8 @@ def residual_log_weights(lp: np.ndarray, lq: np.ndarray) -> np.ndarray:
 
 
 def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int, eos: int,
-           delta: float, b_ids=None, draft_near_tie=None, rule: str = RULE_RATIO, target=None) -> dict:
+           delta: float, b_ids=None, draft_near_tie=None, rule: str = RULE_RATIO, target=None,
+           draft_ids=None) -> dict:
     """O5 for B requests: scan the drafts, stop at the first rejection, emit one more token.
 
     drafts [B][k]; zd_raw [B][k][n_draft] raw draft logits (needed when T > 0);
@@ -377,6 +386,10 @@ def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int
     b_ids = np.arange(B) if b_ids is None else np.asarray(b_ids)
     zv, vflags = sanitize(zv_raw)
     V = zv.shape[-1]
+    # draft row of each vocabulary id (-1 outside the draft vocabulary)
+    row_of = np.full(V, -1, dtype=np.int64)
+    d_ids = np.arange(n_draft) if draft_ids is None else np.asarray(draft_ids, dtype=np.int64)
+    row_of[d_ids] = np.arange(d_ids.size)
     Te = _teff(T)
     lse_v = logsumexp_rows(zv / Te)
     y = argmax_lowest_f32(zv)
@@ -428,10 +441,10 @@ def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int
             mark_tie(active & (ys_margin[:, i] <= delta / T), i)
         elif T > 0:
             lp_t = np.where(t_ok, zv[rows, i, tc] / T - lse_v[:, i], NEG_INF)
-            in_draft = t_ok & (t < n_draft) & ((dflags[:, i] & ROW_INVALID) == 0)
+            tr = row_of[tc]
+            in_draft = t_ok & (tr >= 0) & ((dflags[:, i] & ROW_INVALID) == 0)
             with np.errstate(invalid="ignore"):
-                lq_t = np.where(in_draft, zd[rows, i, np.clip(t, 0, n_draft - 1)] / T - lse_d[:, i],
-                                NEG_INF)
+                lq_t = np.where(in_draft, zd[rows, i, np.maximum(tr, 0)] / T - lse_d[:, i], NEG_INF)
             u = uniform_accept(philox_words(seed, STREAM_ACCEPT, i, b_ids, cycle, 0))
             ok = t_ok & accept_test(lp_t, lq_t, u)
             with np.errstate(invalid="ignore"):
@@ -475,7 +488,7 @@ def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int
         lp = zv[sel, a] / T - lse_v[sel, a][:, None]
         lq = np.full((sel.size, V), NEG_INF)
         dval = (dflags[sel, a] & ROW_INVALID) == 0
-        lq[dval, :n_draft] = zd[sel[dval], a] / T - lse_d[sel[dval], a][:, None]
+        lq[np.ix_(np.nonzero(dval)[0], d_ids)] = zd[sel[dval], a] / T - lse_d[sel[dval], a][:, None]
         ln_r = residual_log_weights(lp, lq)
         G = gumbel_noise(seed, STREAM_RESAMPLE, a, b_ids[sel], cycle, V)
         has_mass = (ln_r > NEG_INF).any(axis=-1)
@@ -557,7 +570,7 @@ def commit(snapshots: np.ndarray, live: np.ndarray, kv: np.ndarray, kv_len: np.n
 # ----------------------------------------------------------------------------------
 def cycle(W64: np.ndarray, n_draft: int, h_d: np.ndarray, h_v: np.ndarray, T: float,
           seed: int, cycle_id: int, eos: int, delta: float, drafts=None, rule: str = RULE_RATIO,
-          positions=None) -> dict:
+          positions=None, draft_ids=None) -> dict:
     """k draft-head calls, one verify over k+1 rows, acceptance [MTP-PR "What"].
 
     h_d [B][k][d], h_v [B][k+1][d] in fp64.  ``drafts`` overrides the draft head's picks
@@ -568,7 +581,7 @@ def cycle(W64: np.ndarray, n_draft: int, h_d: np.ndarray, h_v: np.ndarray, T: fl
     B, k, _ = h_d.shape
     exact = T > 0 and rule == RULE_EXACT
     Td = 0.0 if exact else T
-    dr = [draft_rows(W64, n_draft, h_d[:, i], Td, seed, i, cycle_id, delta) for i in range(k)]
+    dr = [draft_rows(W64, n_draft, h_d[:, i], Td, seed, i, cycle_id, delta, ids=draft_ids) for i in range(k)]
     picked = np.stack([r["token"] for r in dr], axis=1)
     use = picked if drafts is None else np.asarray(drafts, dtype=np.int64)
     dnt = np.stack([r["near_tie"] for r in dr], axis=1)
@@ -577,5 +590,5 @@ def cycle(W64: np.ndarray, n_draft: int, h_d: np.ndarray, h_v: np.ndarray, T: fl
     vr = verify_rows(W64, h_v, use, T, seed, cycle_id, delta, positions=positions if exact else None)
     zd = np.stack([r["logits"] for r in dr], axis=1)
     acc = accept(use, zd, vr["logits"], n_draft, T, seed, cycle_id, eos, delta, draft_near_tie=dnt,
-                 rule=rule, target=vr)
+                 rule=rule, target=vr, draft_ids=draft_ids)
     return dict(drafts=use, draft=dr, verify=vr, accept=acc)

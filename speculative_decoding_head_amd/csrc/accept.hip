@@ -44,10 +44,18 @@ struct Chain {
   uint32_t flags;
 };
 
+// draft row of vocabulary id x (-1: outside the draft vocabulary)
+__device__ __forceinline__ int draft_row(const AcceptLaunch& p, int x) {
+  if (p.draft_row_of) return p.draft_row_of[x];
+  return x < p.n_draft ? x : -1;
+}
+
 __device__ __forceinline__ float draft_logq(const AcceptLaunch& p, int b, int i, int t, float inv_t,
                                             const mtp_row_stats& ds) {
-  if (t < 0 || t >= p.n_draft || (ds.flags & MTP_ROW_INVALID)) return kNegInf;
-  const float z = sanitize(p.dlogits[((size_t)b * p.k_max + i) * p.n_draft + t], ds.flags);
+  if (t < 0 || t >= p.vocab || (ds.flags & MTP_ROW_INVALID)) return kNegInf;
+  const int r = draft_row(p, t);
+  if (r < 0 || r >= p.n_draft) return kNegInf;
+  const float z = sanitize(p.dlogits[((size_t)b * p.k_max + i) * p.n_draft + r], ds.flags);
   return z * inv_t - ds.lse;
 }
 
@@ -143,7 +151,8 @@ __global__ __launch_bounds__(kAcceptThreads) void mtp_accept_sample_kernel(Accep
         const int x = xg + e;
         if (x < x0 || x >= x1) continue;
         const float lp = sanitize(zrow[x], vs.flags) * inv_t - vs.lse;
-        const float lq = (q_valid && x < p.n_draft) ? sanitize(qrow[x], ds.flags) * inv_t - ds.lse : kNegInf;
+        const int dr = q_valid ? draft_row(p, x) : -1;
+        const float lq = (dr >= 0 && dr < p.n_draft) ? sanitize(qrow[dr], ds.flags) * inv_t - ds.lse : kNegInf;
         if (lp > lq) {
           const float lr = lp + log1pf(-__expf(lq - lp));
           if (lr > kNegInf) {

@@ -34,6 +34,7 @@ int check_head(const mtp_head* h, int htype) {
     if (!aligned16(h->scale) || !aligned16(h->minv)) return MTP_ERR_ALIGN;
   }
   if (!aligned16(h->w)) return MTP_ERR_ALIGN;
+  if (h->row_ids && !aligned16(h->row_ids)) return MTP_ERR_ALIGN;
   // weights are addressed with 32-bit buffer offsets: at most 2 GiB per head
   const size_t row = h->wtype == MTP_W_F32 ? (size_t)h->d * 4 : (is_q4(h->wtype) ? (size_t)h->d / 2 : (size_t)h->d * 2);
   const size_t rows = is_tiled(h->wtype) ? (size_t)(h->vocab + 15) / 16 * 16 : (size_t)h->vocab;
@@ -114,6 +115,23 @@ int mtp_pack_head(const mtp_head* src, void* dst_w, void* dst_scale, void* dst_m
                      static_cast<hipStream_t>(stream)) == hipSuccess ? MTP_OK : MTP_ERR_HIP;
 }
 
+int mtp_gather_rows(const mtp_head* src, const int32_t* ids, int32_t n, void* dst_w, void* dst_scale,
+                    void* dst_minv, void* stream) {
+  int st = check_head(src, src && src->wtype == MTP_W_F32 ? MTP_H_F32 : MTP_H_BF16);
+  if (st != MTP_OK) return st;
+  if (src->wtype != MTP_W_F32 && src->wtype != MTP_W_BF16 && src->wtype != MTP_W_Q4A32) return MTP_ERR_DTYPE;
+  if (src->row_ids) return MTP_ERR_SHAPE;
+  if (!ids || !dst_w) return MTP_ERR_NULL;
+  if (n < 1 || n > src->vocab) return MTP_ERR_SHAPE;
+  if (!aligned16(ids) || !aligned16(dst_w)) return MTP_ERR_ALIGN;
+  if (src->wtype == MTP_W_Q4A32) {
+    if (!dst_scale || !dst_minv) return MTP_ERR_NULL;
+    if (!aligned16(dst_scale) || !aligned16(dst_minv)) return MTP_ERR_ALIGN;
+  }
+  return launch_gather(src->wtype, src->w, src->scale, src->minv, src->d, src->vocab, ids, n, dst_w, dst_scale,
+                       dst_minv, static_cast<hipStream_t>(stream)) == hipSuccess ? MTP_OK : MTP_ERR_HIP;
+}
+
 int mtp_draft_head(const mtp_head* head, int32_t n_draft, const void* hidden, int32_t htype,
                    int32_t B, int32_t slot, int32_t k_max, const mtp_sampling* smp,
                    int32_t* draft_tokens, mtp_row_stats* draft_stats, float* draft_logits,
@@ -152,6 +170,7 @@ int mtp_draft_head(const mtp_head* head, int32_t n_draft, const void* hidden, in
   p.cycle = smp->cycle;
   p.request_base = smp->request_base;
   p.positions = nullptr;
+  p.ids = head->row_ids;
   p.inv_t = inv_t_eff(sampled ? smp->temperature : 0.0f);
   p.sampled = sampled;
   p.verify = 0;
@@ -175,6 +194,7 @@ int mtp_verify_logits(const mtp_head* head, const void* hidden, int32_t htype, i
   int st = check_head(head, htype);
   if (st != MTP_OK) return st;
   if ((st = check_sampling(smp)) != MTP_OK) return st;
+  if (head->row_ids) return MTP_ERR_SHAPE;   // the verify scores the whole vocabulary
   if (!hidden || !draft_tokens || !row_stats) return MTP_ERR_NULL;
   if (k < 1 || k > kMaxK || k_max < k || k_max > kMaxK) return MTP_ERR_SHAPE;
   if (B < 1) return MTP_ERR_SHAPE;
@@ -209,6 +229,7 @@ int mtp_verify_logits(const mtp_head* head, const void* hidden, int32_t htype, i
   p.cycle = smp->cycle;
   p.request_base = smp->request_base;
   p.positions = exact ? smp->positions : nullptr;
+  p.ids = nullptr;
   p.inv_t = inv_t_eff(smp->temperature);
   p.sampled = sampled;
   p.verify = 1;
@@ -230,7 +251,7 @@ int mtp_verify_logits(const mtp_head* head, const void* hidden, int32_t htype, i
 int mtp_accept_sample(int32_t B, int32_t k, int32_t k_max, int32_t vocab, int32_t n_draft,
                       const mtp_sampling* smp, const int32_t* draft_tokens,
                       const mtp_row_stats* draft_stats, const float* draft_logits,
-                      const mtp_row_stats* row_stats, const float* logits,
+                      const mtp_row_stats* row_stats, const float* logits, const int32_t* draft_row_of,
                       int32_t* out_tokens, int32_t* n_accept, int32_t* n_emit, uint32_t* flags,
                       void* ws, size_t ws_bytes, void* stream) {
   int st = check_sampling(smp);
@@ -243,6 +264,7 @@ int mtp_accept_sample(int32_t B, int32_t k, int32_t k_max, int32_t vocab, int32_
   const bool ratio = ratio_sampling(smp);
   if (ratio && (!draft_logits || !logits)) return MTP_ERR_NULL;
   if (!aligned16(draft_stats) || !aligned16(row_stats)) return MTP_ERR_ALIGN;
+  if (draft_row_of && !aligned16(draft_row_of)) return MTP_ERR_ALIGN;
   const size_t need = accept_ws_bytes(B, vocab, ratio);
   if (need > 0) {
     if (!ws) return MTP_ERR_WORKSPACE;
@@ -267,6 +289,7 @@ int mtp_accept_sample(int32_t B, int32_t k, int32_t k_max, int32_t vocab, int32_
   p.dlogits = draft_logits;
   p.vstats = row_stats;
   p.vlogits = logits;
+  p.draft_row_of = draft_row_of;
   p.out_tokens = out_tokens;
   p.n_accept = n_accept;
   p.n_emit = n_emit;

@@ -37,6 +37,7 @@ struct LmheadLaunch {
   uint32_t key0, key1, cycle, request_base;
   const int32_t* positions;   // verify with exact-match acceptance at T > 0: [B] position of
                               // row 0; the sample then comes from the position-keyed stream 3
+  const int32_t* ids;         // draft head gathered from a set of ids: vocabulary id of each row
   float inv_t;            // 1 / T_eff
   int sampled;            // T > 0
   int verify;             // 1: verify pass, 0: draft head
@@ -72,6 +73,7 @@ struct AcceptLaunch {
   const float* dlogits;
   const mtp_row_stats* vstats;
   const float* vlogits;
+  const int32_t* draft_row_of;   // [vocab] draft row of each id, or -1; NULL: rows are ids 0..n_draft-1
   int32_t* out_tokens;
   int32_t* n_accept;
   int32_t* n_emit;
@@ -97,6 +99,8 @@ struct CommitLaunch {
 hipError_t launch_commit(const CommitLaunch& p, hipStream_t stream);
 
 size_t tiled_bytes(int wtype, int d, int vocab, int part);   // source wtype BF16 or Q4A32
+hipError_t launch_gather(int wtype, const void* w, const void* scale, const void* minv, int d, int vocab,
+                         const int32_t* ids, int n, void* dst_w, void* dst_scale, void* dst_minv, hipStream_t stream);
 hipError_t launch_pack(int wtype, const void* w, const void* scale, const void* minv, int d, int vocab,
                        void* dst_w, void* dst_scale, void* dst_minv, hipStream_t stream);
 

@@ -287,6 +287,9 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
     for (int t = 0; t < TV; ++t) {
       const int x = (tb + t) * 16 + xi;
       if ((tb + t) >= t_end || x >= p.n_rows) continue;
+      // a draft head gathered from a set of ids: its row x stands for vocabulary id
+      // ids[x]; ids and draws refer to the vocabulary, the stored logits to the row
+      const int xv = (!VERIFY && p.ids) ? p.ids[x] : x;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (!rvalid[r]) continue;
@@ -294,11 +297,11 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
         const float z = c[t][r];
         float gn = 0.0f;
         if (SAMPLED) {
-          const u32x4 wd = philox4x32_10(u32x4{(uint32_t)x >> 2, prow[r], preq[r], pcyc[r]}, p.key0, p.key1);
-          const int sel = x & 3;
+          const u32x4 wd = philox4x32_10(u32x4{(uint32_t)xv >> 2, prow[r], preq[r], pcyc[r]}, p.key0, p.key1);
+          const int sel = xv & 3;
           gn = gumbel_from_word(sel == 0 ? wd.x : (sel == 1 ? wd.y : (sel == 2 ? wd.z : wd.w)));
         }
-        rowacc_push<SAMPLED>(acc[r], z, x, p.inv_t, gn);
+        rowacc_push<SAMPLED>(acc[r], z, xv, p.inv_t, gn);
         if (p.logits) p.logits[(long long)j * p.logits_stride + x] = z;
         if (VERIFY && x == tok[r])
           store_coherent(reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(p.ws) + 256) + j, __float_as_uint(z));

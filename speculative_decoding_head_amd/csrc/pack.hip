@@ -76,6 +76,35 @@ size_t tiled_bytes(int wtype, int d, int vocab, int part) {
   return 0;
 }
 
+// gather: one block per output row; row r <- row ids[r] of the source (zeros for an id
+// outside [0, vocab)); for 4-bit heads also the row's scales and mins
+__global__ __launch_bounds__(kPackThreads) void gather_rows_kernel(const unsigned char* src, unsigned char* dst,
+                                                                  size_t row_bytes, const int32_t* ids, int vocab) {
+  const int r = blockIdx.x;
+  const int id = ids[r];
+  const bool ok = id >= 0 && id < vocab;
+  const u32x4* s = reinterpret_cast<const u32x4*>(src + (ok ? (size_t)id : 0) * row_bytes);
+  u32x4* o = reinterpret_cast<u32x4*>(dst + (size_t)r * row_bytes);
+  for (size_t v = threadIdx.x; v < row_bytes / 16; v += kPackThreads) o[v] = ok ? s[v] : u32x4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_gather(int wtype, const void* w, const void* scale, const void* minv, int d, int vocab,
+                         const int32_t* ids, int n, void* dst_w, void* dst_scale, void* dst_minv, hipStream_t stream) {
+  const size_t rb = wtype == MTP_W_F32 ? (size_t)d * 4 : (wtype == MTP_W_BF16 ? (size_t)d * 2 : (size_t)d / 2);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(n), dim3(kPackThreads), 0, stream, static_cast<const unsigned char*>(w),
+                     static_cast<unsigned char*>(dst_w), rb, ids, vocab);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || wtype != MTP_W_Q4A32) return e;
+  const size_t sb = (size_t)(d / 32) * 2;   // bf16 per 32-value group
+  for (int part = 0; part < 2; ++part) {
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(n), dim3(kPackThreads), 0, stream,
+                       static_cast<const unsigned char*>(part ? minv : scale),
+                       static_cast<unsigned char*>(part ? dst_minv : dst_scale), sb, ids, vocab);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_pack(int wtype, const void* w, const void* scale, const void* minv, int d, int vocab,
                        void* dst_w, void* dst_scale, void* dst_minv, hipStream_t stream) {
   if (wtype == MTP_W_BF16) {

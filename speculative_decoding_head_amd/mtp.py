@@ -32,7 +32,7 @@ ACCEPT_RATIO, ACCEPT_EXACT = 0, 1
 EXPORTED = ("mtp_draft_head", "mtp_verify_logits", "mtp_accept_sample", "mtp_commit_state",
             "mtp_workspace_bytes", "mtp_tiled_bytes", "mtp_pack_head", "mtp_status_str", "mtp_abi_version",
             "mtp_width_init", "mtp_width_observe", "mtp_width_expected_tokens", "mtp_width_cost",
-            "mtp_width_choose")
+            "mtp_width_choose", "mtp_gather_rows")
 
 
 class MtpError(RuntimeError):
@@ -50,7 +50,7 @@ class _WidthCtl(ctypes.Structure):
 class _Head(ctypes.Structure):
     _fields_ = [("wtype", ctypes.c_int32), ("d", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("w", ctypes.c_void_p), ("scale", ctypes.c_void_p),
-                ("minv", ctypes.c_void_p)]
+                ("minv", ctypes.c_void_p), ("row_ids", ctypes.c_void_p)]
 
 
 class _Sampling(ctypes.Structure):
@@ -74,7 +74,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     hp, sp = ctypes.POINTER(_Head), ctypes.POINTER(_Sampling)
     lib.mtp_draft_head.argtypes = [hp, i32, vp, i32, i32, i32, i32, sp, vp, vp, vp, vp, sz, vp]
     lib.mtp_verify_logits.argtypes = [hp, vp, i32, i32, i32, vp, i32, sp, vp, vp, vp, sz, vp]
-    lib.mtp_accept_sample.argtypes = [i32, i32, i32, i32, i32, sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.mtp_accept_sample.argtypes = [i32, i32, i32, i32, i32, sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.mtp_gather_rows.argtypes = [hp, vp, i32, vp, vp, vp, vp]
+    lib.mtp_gather_rows.restype = ctypes.c_int
     lib.mtp_commit_state.argtypes = [i32, i32, vp, vp, vp, sz, vp, i32, i32, sz, vp, vp]
     for f in ("mtp_draft_head", "mtp_verify_logits", "mtp_accept_sample", "mtp_commit_state", "mtp_abi_version"):
         getattr(lib, f).restype = ctypes.c_int
@@ -148,10 +150,12 @@ class Head:
     w: torch.Tensor
     scale: Optional[torch.Tensor] = None
     minv: Optional[torch.Tensor] = None
+    row_ids: Optional[torch.Tensor] = None   # int32 [vocab]: vocabulary id of each row (gathered draft heads)
 
     def _struct(self) -> _Head:
         return _Head(self.wtype, self.d, self.vocab, 0, _ptr(self.w, name="w"),
-                     _ptr(self.scale, name="scale"), _ptr(self.minv, name="minv"))
+                     _ptr(self.scale, name="scale"), _ptr(self.minv, name="minv"),
+                     _ptr(self.row_ids, (torch.int32,), "row_ids"))
 
 
 def sampling(temperature: float = 0.0, eos_id: int = -1, seed: int = 0, cycle: int = 0,
@@ -210,7 +214,27 @@ def tiled_head(src: Head, stream=None) -> Head:
     sc = torch.empty(nb[1], dtype=torch.uint8, device=dev) if nb[1] else None
     mn = torch.empty(nb[2], dtype=torch.uint8, device=dev) if nb[2] else None
     mtp_pack_head(src, w, sc, mn, stream)
-    return Head(W_BF16_TILED if src.wtype == W_BF16 else W_Q4A32_TILED, src.d, src.vocab, w, sc, mn)
+    return Head(W_BF16_TILED if src.wtype == W_BF16 else W_Q4A32_TILED, src.d, src.vocab, w, sc, mn, src.row_ids)
+
+
+def gather_rows(src: Head, ids: torch.Tensor, stream=None) -> Head:
+    """mtp_gather_rows: a row-major head of the rows ``ids`` (device int32, strictly
+    ascending) of the row-major head ``src``, with row_ids = ids."""
+    if src.wtype not in (W_F32, W_BF16, W_Q4A32):
+        raise MtpError("gather from a row-major head")
+    n = int(ids.numel())
+    dev = src.w.device
+    if src.wtype == W_Q4A32:
+        w = torch.empty(n, src.d // 2, dtype=torch.uint8, device=dev)
+        sc = torch.empty(n, src.d // 32, dtype=torch.int16, device=dev)
+        mn = torch.empty(n, src.d // 32, dtype=torch.int16, device=dev)
+    else:
+        w = torch.empty(n, src.d, dtype=torch.float32 if src.wtype == W_F32 else torch.int16, device=dev)
+        sc = mn = None
+    h = src._struct()
+    _check(load_library().mtp_gather_rows(ctypes.byref(h), _ptr(ids, (torch.int32,), "ids"), n, _ptr(w, name="w"),
+                                          _ptr(sc, name="scale"), _ptr(mn, name="minv"), _stream(stream)))
+    return Head(src.wtype, src.d, n, w, sc, mn, ids)
 
 
 # ---------------------------------------------------------------------------------
@@ -246,7 +270,7 @@ def mtp_accept_sample(B: int, k: int, k_max: int, vocab: int, n_draft: int, smp:
                       draft_tokens: torch.Tensor, draft_stats: torch.Tensor, draft_logits: Optional[torch.Tensor],
                       row_stats: torch.Tensor, logits: Optional[torch.Tensor], out_tokens: torch.Tensor,
                       n_accept: torch.Tensor, n_emit: torch.Tensor, flags: torch.Tensor,
-                      ws: Optional[torch.Tensor], stream=None) -> None:
+                      ws: Optional[torch.Tensor], stream=None, draft_row_of: Optional[torch.Tensor] = None) -> None:
     lib = load_library()
     _check(lib.mtp_accept_sample(int(B), int(k), int(k_max), int(vocab), int(n_draft), ctypes.byref(smp),
                                  _ptr(draft_tokens, (torch.int32,), "draft_tokens"),
@@ -254,6 +278,7 @@ def mtp_accept_sample(B: int, k: int, k_max: int, vocab: int, n_draft: int, smp:
                                  _ptr(draft_logits, (torch.float32,), "draft_logits"),
                                  _ptr(row_stats, (torch.int32,), "row_stats"),
                                  _ptr(logits, (torch.float32,), "logits"),
+                                 _ptr(draft_row_of, (torch.int32,), "draft_row_of"),
                                  _ptr(out_tokens, (torch.int32,), "out_tokens"),
                                  _ptr(n_accept, (torch.int32,), "n_accept"), _ptr(n_emit, (torch.int32,), "n_emit"),
                                  _ptr(flags, (torch.int32,), "flags"),

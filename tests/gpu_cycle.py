@@ -44,8 +44,14 @@ class GpuCycle:
     """Device buffers for one cycle of B requests with k drafts."""
 
     def __init__(self, dhead: mtp.Head, n_draft: int, B: int, k: int, temperature: float, seed: int = 0,
-                 eos: int = -1, k_max: int | None = None, rule: int = mtp.ACCEPT_RATIO):
+                 eos: int = -1, k_max: int | None = None, rule: int = mtp.ACCEPT_RATIO,
+                 draft_head: mtp.Head | None = None, draft_row_of: torch.Tensor | None = None):
+        """``draft_head``: a head gathered from a set of ids (row_ids set) for the draft
+        calls, with ``draft_row_of`` its inverse map; default: the first n_draft rows of
+        ``dhead``."""
         self.h, self.n_draft, self.B, self.k = dhead, n_draft, B, k
+        self.dh = dhead if draft_head is None else draft_head
+        self.row_of = draft_row_of
         self.rule = rule
         self.positions = torch.zeros(B, dtype=torch.int32, device="cuda")
         self.k_max = k if k_max is None else k_max
@@ -75,7 +81,7 @@ class GpuCycle:
         return mtp.sampling(self.T, self.eos, self.seed, cycle, request_base, self.rule, self.positions)
 
     def draft(self, slot: int, h_slot: torch.Tensor, cycle=0, request_base=0):
-        mtp.mtp_draft_head(self.h, self.n_draft, h_slot, slot, self.k_max, self.smp(cycle, request_base),
+        mtp.mtp_draft_head(self.dh, self.n_draft, h_slot, slot, self.k_max, self.smp(cycle, request_base),
                            self.draft_tokens, self.draft_stats, self.draft_logits, self.ws)
 
     def verify(self, h_v: torch.Tensor, cycle=0, request_base=0):
@@ -85,7 +91,8 @@ class GpuCycle:
     def accept(self, cycle=0, request_base=0):
         mtp.mtp_accept_sample(self.B, self.k, self.k_max, self.h.vocab, self.n_draft, self.smp(cycle, request_base),
                               self.draft_tokens, self.draft_stats, self.draft_logits, self.row_stats, self.logits,
-                              self.out_tokens, self.n_accept, self.n_emit, self.flags, self.ws)
+                              self.out_tokens, self.n_accept, self.n_emit, self.flags, self.ws,
+                              draft_row_of=self.row_of)
 
     def run(self, h_d: torch.Tensor, h_v: torch.Tensor, cycle=0, request_base=0, drafts=None) -> dict:
         """h_d [B][k][d], h_v [B][k+1][d] on the device."""

@@ -161,6 +161,7 @@ def test_sampling_struct_layout():
     (dict(out=None), -1), (dict(temperature=1.0, logits=None), -1),
     (dict(temperature=1.0, ws=None), -6),
     (dict(temperature=1.0, ws_bytes=10), -6),
+    (dict(row_of=FAKE + 4), -5),
 ])
 def test_accept_rejects_bad_arguments(lib, case, want):
     a = dict(B=1, k=3, k_max=3, vocab=152064, n_draft=64000, out=FAKE, logits=FAKE, temperature=0.0, ws=FAKE,
@@ -168,7 +169,8 @@ def test_accept_rejects_bad_arguments(lib, case, want):
     a.update(case)
     smp = mtp.sampling(a["temperature"])
     r = lib.mtp_accept_sample(a["B"], a["k"], a["k_max"], a["vocab"], a["n_draft"], ctypes.byref(smp), FAKE, FAKE,
-                              FAKE, FAKE, a["logits"], a["out"], FAKE, FAKE, FAKE, a["ws"], a["ws_bytes"], None)
+                              FAKE, FAKE, a["logits"], a.get("row_of"), a["out"], FAKE, FAKE, FAKE, a["ws"],
+                              a["ws_bytes"], None)
     assert r == want
 
 
@@ -190,3 +192,23 @@ def test_binding_refuses_host_tensors():
         pytest.skip("libmtp.so not built")
     with pytest.raises(mtp.MtpError):
         mtp.mtp._ptr(torch.zeros(4), name="x")
+
+
+@pytest.mark.parametrize("case,want", [
+    (dict(ids=None), -1), (dict(dst=None), -1), (dict(n=0), -2), (dict(n=5000), -2),
+    (dict(ids=FAKE + 4), -5), (dict(wtype=mtp.W_BF16_TILED), -3), (dict(row_ids=FAKE), -2),
+])
+def test_gather_rejects_bad_arguments(lib, case, want):
+    a = dict(ids=FAKE, dst=FAKE, n=16, wtype=mtp.W_BF16, row_ids=None)
+    a.update(case)
+    head = mtp.mtp._Head(a["wtype"], 256, 4096, 0, FAKE, None, None, a["row_ids"])
+    r = lib.mtp_gather_rows(ctypes.byref(head), a["ids"], a["n"], a["dst"], None, None, None)
+    assert r == want
+
+
+def test_verify_rejects_a_head_with_row_ids(lib):
+    head = mtp.mtp._Head(mtp.W_BF16, 256, 4096, 0, FAKE, None, None, FAKE)
+    smp = mtp.sampling(0.0)
+    r = lib.mtp_verify_logits(ctypes.byref(head), FAKE, mtp.H_BF16, 1, 3, FAKE, 3, ctypes.byref(smp), FAKE, None,
+                              FAKE, 1 << 24, None)
+    assert r == -2
