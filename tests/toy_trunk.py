@@ -53,3 +53,56 @@ class ToyTrunk:
     @staticmethod
     def state_bytes(S: np.ndarray) -> np.ndarray:
         return np.frombuffer(np.ascontiguousarray(S, dtype=np.float64).tobytes(), dtype=np.uint8).copy()
+
+
+class ToyTrunkConv(ToyTrunk):
+    """The toy trunk with a short causal convolution in front of each recurrent update
+    (as the gated-delta layers of the pages' model have): the state is the matrices S plus
+    the last C inputs, so rolling back needs the conv rows too.  State = one float64
+    vector [vec(S), conv rows], padded to a whole number of 16-byte words."""
+
+    def __init__(self, seed: int, C: int = 3, **kw):
+        super().__init__(seed, **kw)
+        rng = np.random.default_rng(seed + 1000)
+        self.C = C
+        self.cw = rng.standard_normal(C) / C + np.eye(1, C, C - 1)[0]      # last tap dominant
+        self.ns = self.H * self.n * self.n
+        self.size = self.ns + C * self.d
+        self.size += self.size % 2
+
+    def zero_state(self) -> np.ndarray:
+        return np.zeros(self.size)
+
+    def _split(self, st):
+        S = st[:self.ns].reshape(self.H, self.n, self.n)
+        conv = st[self.ns:self.ns + self.C * self.d].reshape(self.C, self.d)
+        return S, conv
+
+    def step(self, st: np.ndarray, tok: int) -> np.ndarray:
+        S, conv = self._split(st)
+        conv = np.concatenate([conv[1:], self.E[tok][None]], axis=0)
+        x = self.cw @ conv                                                 # short conv over the inputs
+        S = S.copy()
+        for h in range(self.H):
+            kappa = self.Ak[h] @ x
+            kappa /= max(np.linalg.norm(kappa), 1e-12)
+            v = self.Av[h] @ x
+            beta = 1.0 / (1.0 + np.exp(-(self.c[h] @ x)))
+            S[h] = 0.97 * S[h] @ self.Q[h] + beta * np.outer(v - S[h] @ kappa, kappa)
+        out = np.zeros(self.size)
+        out[:self.ns] = S.reshape(-1)
+        out[self.ns:self.ns + self.C * self.d] = conv.reshape(-1)
+        return out
+
+    def hidden(self, st: np.ndarray, tok: int, drafter: bool = False) -> np.ndarray:
+        S, conv = self._split(st)
+        P = self.Pd if drafter else self.P
+        return np.tanh(P @ S.reshape(-1) - 1.2 * (self.cw @ conv))
+
+    @staticmethod
+    def state_bytes(st: np.ndarray) -> np.ndarray:
+        return np.frombuffer(np.ascontiguousarray(st, dtype=np.float64).tobytes(), dtype=np.uint8).copy()
+
+    @staticmethod
+    def from_bytes(b: np.ndarray) -> np.ndarray:
+        return np.frombuffer(np.ascontiguousarray(b).tobytes(), dtype=np.float64).copy()
