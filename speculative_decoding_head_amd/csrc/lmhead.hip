@@ -336,7 +336,7 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   if (tid < M) {
     RowAcc a = red[tid];
     for (int w = 1; w < kWaves; ++w) rowacc_merge(a, red[w * 16 + tid]);
-    store_partial(pr, (uint32_t)(((size_t)blockIdx.x * M + tid) * sizeof(RowAcc)), a);
+    store_partial_fm(pr, tid, blockIdx.x, M, G, a);
   }
   wait_stores();
   __syncthreads();
@@ -357,7 +357,7 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
 #pragma unroll
     for (int q = 0; q < kMaxGrid / 64; ++q) {
       const int blk = lane + 64 * q;
-      if (j < M && blk < G) part[jj][q] = load_partial(pr, (uint32_t)(((size_t)blk * M + j) * sizeof(RowAcc)));
+      if (j < M && blk < G) part[jj][q] = load_partial_fm(pr, j, blk, M, G);
       else rowacc_init(part[jj][q]);
     }
     zbits[jj] = (VERIFY && j < M) ? load_coherent(reinterpret_cast<const uint32_t*>(ztok) + j) : 0u;

@@ -83,16 +83,21 @@ __device__ __forceinline__ size_t row_bytes(int d) {
 
 // partials are handed between blocks as three 16-byte device-scope buffer stores/loads
 constexpr int kCoherent = 16;   // cache-policy bits: device scope (sc1)
-__device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t r, uint32_t off, const RowAcc& a) {
+// field-major partials: 16-byte piece i of (row j, block b) at ((i * M + j) * G + b) * 16,
+// so that lanes reading consecutive blocks of one row read contiguous bytes
+__device__ __forceinline__ uint32_t partial_piece_off(int i, int j, int b, int M, int G) {
+  return (uint32_t)((((size_t)i * M + j) * G + b) * 16);
+}
+__device__ __forceinline__ void store_partial_fm(__amdgpu_buffer_rsrc_t r, int j, int b, int M, int G, const RowAcc& a) {
   const u32x4* v = reinterpret_cast<const u32x4*>(&a);
 #pragma unroll
-  for (int i = 0; i < 3; ++i) __builtin_amdgcn_raw_buffer_store_b128(v[i], r, (int)(off + 16 * i), 0, kCoherent);
+  for (int i = 0; i < 3; ++i) __builtin_amdgcn_raw_buffer_store_b128(v[i], r, (int)partial_piece_off(i, j, b, M, G), 0, kCoherent);
 }
-__device__ __forceinline__ RowAcc load_partial(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+__device__ __forceinline__ RowAcc load_partial_fm(__amdgpu_buffer_rsrc_t r, int j, int b, int M, int G) {
   RowAcc a;
   u32x4* v = reinterpret_cast<u32x4*>(&a);
 #pragma unroll
-  for (int i = 0; i < 3; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16 * i), 0, kCoherent);
+  for (int i = 0; i < 3; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)partial_piece_off(i, j, b, M, G), 0, kCoherent);
   return a;
 }
 

@@ -741,8 +741,12 @@ __device__ __forceinline__ void wide_body(const LmheadLaunch& p) {
   if (tid < M) {
     RowAcc a = lrun[tid];
     for (int w = 1; w < kWaves; ++w) rowacc_merge(a, lrun[w * kRows + tid]);
-    RowAcc* partials = reinterpret_cast<RowAcc*>(static_cast<unsigned char*>(p.ws) + lmhead_partials_offset(M));
-    partials[(size_t)blockIdx.x * M + tid] = a;
+    // field-major: 16-byte piece i of (row, block) at [i][row][block], so the merge's
+    // lanes (consecutive blocks of one row) read contiguous bytes
+    u32x4* pf = reinterpret_cast<u32x4*>(static_cast<unsigned char*>(p.ws) + lmhead_partials_offset(M));
+    const u32x4* av = reinterpret_cast<const u32x4*>(&a);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) pf[((size_t)i * M + tid) * gridDim.x + blockIdx.x] = av[i];
   }
 }
 
@@ -754,10 +758,16 @@ __device__ __forceinline__ void wide_merge_body(const LmheadLaunch& p, int G) {
   const int j = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int M = p.M;
   const unsigned char* ws = static_cast<const unsigned char*>(p.ws);
-  const RowAcc* partials = reinterpret_cast<const RowAcc*>(ws + lmhead_partials_offset(M));
+  const u32x4* pf = reinterpret_cast<const u32x4*>(ws + lmhead_partials_offset(M));
   RowAcc a;
   rowacc_init(a);
-  for (int blk = tid; blk < G; blk += kMergeThreads) rowacc_merge(a, partials[(size_t)blk * M + j]);
+  for (int blk = tid; blk < G; blk += kMergeThreads) {
+    RowAcc b;
+    u32x4* bv = reinterpret_cast<u32x4*>(&b);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) bv[i] = pf[((size_t)i * M + j) * G + blk];
+    rowacc_merge(a, b);
+  }
 #pragma unroll
   for (int mask = 1; mask < 64; mask <<= 1) {
     const RowAcc o = rowacc_shfl_xor(a, mask);
