@@ -344,46 +344,64 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   __syncthreads();
   if (!*last_flag) return;
 
-  // ---- last block: one wave per row merges the per-block partials in block order.
-  //      These loads bypass the caches and each round trip is long, so every load a wave
-  //      needs (the partials of its rows, the drafted-id logits) goes out before the first
-  //      merge.  M <= kLmheadMaxRows, so a wave has at most kRowsPerWave rows.
-  constexpr int kRowsPerWave = (kLmheadMaxRows + kWaves - 1) / kWaves;
-  RowAcc part[kRowsPerWave][kMaxGrid / 64];
-  uint32_t zbits[kRowsPerWave];
+  // ---- last block: wave w merges rows w and w + 8 (M <= 16): 4 partials per lane in
+  //      block order, then a butterfly over the 64 lanes (DPP inside rows of 16, exchanges
+  //      across them).  One fixed tree for every row and every M, so a row's statistics do
+  //      not depend on the launch size.  The two rows' chains are interleaved step by step,
+  //      and every partial load (and the drafted-id logit) goes out before the first merge:
+  //      these loads bypass the caches and each round trip is long.
+  static_assert(kLmheadMaxRows <= 2 * kWaves && kMaxGrid <= 4 * 64, "two rows per wave, 4 partials per lane");
+  {
+    constexpr int NP = kMaxGrid / 64;
+    const int jr[2] = {wave, wave + kWaves};
+    RowAcc part[2][NP];
+    uint32_t zbits[2];
 #pragma unroll
-  for (int jj = 0; jj < kRowsPerWave; ++jj) {
-    const int j = wave + jj * kWaves;
+    for (int r = 0; r < 2; ++r) {
 #pragma unroll
-    for (int q = 0; q < kMaxGrid / 64; ++q) {
-      const int blk = lane + 64 * q;
-      if (j < M && blk < G) part[jj][q] = load_partial_fm(pr, j, blk, M, G);
-      else rowacc_init(part[jj][q]);
+      for (int q = 0; q < NP; ++q) {
+        const int blk = lane + 64 * q;
+        if (jr[r] < M && blk < G) part[r][q] = load_partial_fm(pr, jr[r], blk, M, G);
+        else rowacc_init(part[r][q]);
+      }
+      zbits[r] = (VERIFY && jr[r] < M) ? load_coherent(reinterpret_cast<const uint32_t*>(ztok) + jr[r]) : 0u;
     }
-    zbits[jj] = (VERIFY && j < M) ? load_coherent(reinterpret_cast<const uint32_t*>(ztok) + j) : 0u;
-  }
+    RowAcc a[2] = {part[0][0], part[1][0]};
+    const bool two = jr[1] < M;   // wave-uniform: the second chain only when it has a row
 #pragma unroll
-  for (int jj = 0; jj < kRowsPerWave; ++jj) {
-    const int j = wave + jj * kWaves;
-    if (j >= M) continue;   // wave-uniform
-    RowAcc a = part[jj][0];
-#pragma unroll
-    for (int q = 1; q < kMaxGrid / 64; ++q) rowacc_merge(a, part[jj][q]);
-#pragma unroll
-    for (int mask = 1; mask < 64; mask <<= 1) {
-      const RowAcc o = rowacc_shfl_xor(a, mask);
-      rowacc_merge(a, o);
+    for (int q = 1; q < NP; ++q) {
+      rowacc_merge(a[0], part[0][q]);
+      if (two) rowacc_merge(a[1], part[1][q]);
     }
-    if (lane == 0) {
-      mtp_row_stats st = finalize_row(a, SAMPLED);
+    // one butterfly step on both chains; the exchange reads a lane's partner before
+    // either merge writes
+    auto bfly = [&](auto xchg) {
+      const RowAcc o0 = xchg(a[0]);
+      if (two) {
+        const RowAcc o1 = xchg(a[1]);
+        rowacc_merge(a[1], o1);
+      }
+      rowacc_merge(a[0], o0);
+    };
+    bfly([](const RowAcc& x) { return rowacc_xor16<1>(x); });
+    bfly([](const RowAcc& x) { return rowacc_xor16<2>(x); });
+    bfly([](const RowAcc& x) { return rowacc_xor16<4>(x); });
+    bfly([](const RowAcc& x) { return rowacc_xor16<8>(x); });
+    bfly([](const RowAcc& x) { return rowacc_shfl_xor(x, 16); });
+    bfly([](const RowAcc& x) { return rowacc_shfl_xor(x, 32); });
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int j = jr[r];
+      if (j >= M || lane != 0) continue;
+      mtp_row_stats st = finalize_row(a[r], SAMPLED);
       const uint32_t fl = st.flags;
       if (VERIFY) {
         const int b = j / p.rows_per_req, i = j % p.rows_per_req;
         const int t = (i < p.k) ? p.drafts[(size_t)b * p.k_max + i] : -1;
-        st.z_tok = (t >= 0 && t < p.n_rows && !(fl & MTP_ROW_INVALID)) ? sanitize(__uint_as_float(zbits[jj]), fl)
+        st.z_tok = (t >= 0 && t < p.n_rows && !(fl & MTP_ROW_INVALID)) ? sanitize(__uint_as_float(zbits[r]), fl)
                                                                          : kNegInf;
       } else {
-        st.z_tok = (fl & MTP_ROW_POSINF) ? 0.0f : ((fl & MTP_ROW_INVALID) ? kNegInf : (SAMPLED ? a.gz : a.zmax));
+        st.z_tok = (fl & MTP_ROW_POSINF) ? 0.0f : ((fl & MTP_ROW_INVALID) ? kNegInf : (SAMPLED ? a[r].gz : a[r].zmax));
         p.tokens[(size_t)j * p.k_max + p.row_base] = st.sample;
       }
       p.stats[(size_t)j * p.out_stride + p.out_offset] = st;
