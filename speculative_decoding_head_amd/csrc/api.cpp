@@ -313,7 +313,7 @@ int mtp_commit_state(int32_t B, int32_t k, const int32_t* n_accept, const void* 
     if (!aligned16(kv)) return MTP_ERR_ALIGN;
   }
   if ((snapshots && !aligned16(snapshots)) || (live && !aligned16(live))) return MTP_ERR_ALIGN;
-  if (state_bytes / (64 * 1024) >= 0x7fffffff) return MTP_ERR_SHAPE;
+  if (state_bytes / (16 * 1024) >= 0x7fffffff) return MTP_ERR_SHAPE;   // grid.x of the commit
   CommitLaunch p{};
   p.B = B;
   p.k = k;
