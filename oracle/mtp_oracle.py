@@ -440,7 +440,8 @@ def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int
             ok = t_ok & (t == ys[:, i])
             mark_tie(active & (ys_margin[:, i] <= delta / T), i)
         elif T > 0:
-            lp_t = np.where(t_ok, zv[rows, i, tc] / T - lse_v[:, i], NEG_INF)
+            with np.errstate(invalid="ignore"):   # a non-finite target row gives NaN here, flagged above
+                lp_t = np.where(t_ok, zv[rows, i, tc] / T - lse_v[:, i], NEG_INF)
             tr = row_of[tc]
             in_draft = t_ok & (tr >= 0) & ((dflags[:, i] & ROW_INVALID) == 0)
             with np.errstate(invalid="ignore"):
