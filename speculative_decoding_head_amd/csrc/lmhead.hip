@@ -164,6 +164,9 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   };
   f32x4 c[TV];
   auto comp = [&](const Chunk& ck, int s0) {
+    // 4-bit heads: d is a multiple of 256 and a chunk a multiple of 8 K steps, so a chunk
+    // is either inside K or wholly past it (wave-uniform)
+    if (L::q4 && s0 >= nsteps) return;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = s0 + u;
@@ -185,22 +188,20 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
         }
       } else {
         // 4-bit affine: D = sum (128 + q) h over the group, then z += s D + (min - 128 s) sum(h)
-        if (s < nsteps) {
-          const f32x4 hs = *reinterpret_cast<const f32x4*>(htab + s * 16 + 4 * g);
+        const f32x4 hs = *reinterpret_cast<const f32x4*>(htab + s * 16 + 4 * g);
 #pragma unroll
-          for (int t = 0; t < TV; ++t) {
-            const f32x4 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                as_bf16x8(a), as_bf16x8(q4_expand(ck.w[t][u])), f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-            const uint4 sq = ck.sc[t][u / 8], mq = ck.mn[t][u / 8];
-            const int uo = u % 8;
-            const uint32_t sw = (uo < 2) ? sq.x : (uo < 4) ? sq.y : (uo < 6) ? sq.z : sq.w;
-            const uint32_t mw = (uo < 2) ? mq.x : (uo < 4) ? mq.y : (uo < 6) ? mq.z : mq.w;
-            const float sv = bf16_to_f32((uint16_t)((u & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
-            const float mv = bf16_to_f32((uint16_t)((u & 1) ? (mw >> 16) : (mw & 0xFFFFu)));
-            const float off = mv - 128.0f * sv;
+        for (int t = 0; t < TV; ++t) {
+          const f32x4 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(a), as_bf16x8(q4_expand(ck.w[t][u])), f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+          const uint4 sq = ck.sc[t][u / 8], mq = ck.mn[t][u / 8];
+          const int uo = u % 8;
+          const uint32_t sw = (uo < 2) ? sq.x : (uo < 4) ? sq.y : (uo < 6) ? sq.z : sq.w;
+          const uint32_t mw = (uo < 2) ? mq.x : (uo < 4) ? mq.y : (uo < 6) ? mq.z : mq.w;
+          const float sv = bf16_to_f32((uint16_t)((u & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+          const float mv = bf16_to_f32((uint16_t)((u & 1) ? (mw >> 16) : (mw & 0xFFFFu)));
+          const float off = mv - 128.0f * sv;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) c[t][r] = fmaf(off, hs[r], fmaf(sv, D[r], c[t][r]));
-          }
+          for (int r = 0; r < 4; ++r) c[t][r] = fmaf(off, hs[r], fmaf(sv, D[r], c[t][r]));
         }
       }
     }

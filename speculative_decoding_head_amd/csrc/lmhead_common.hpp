@@ -42,11 +42,13 @@ template <int WT> struct Layout {
 
 // eight 4-bit codes (element 2m in the low nibble of byte m) -> bf16 values 128 + q, in
 // the lane order [q0, q2, q1, q3, q4, q6, q5, q7]
+// (bf16 128 + q is 0x4300 | q).  The low and high nibbles of the four bytes are masked
+// out, then each byte permute puts two of them under the exponent byte 0x43: 7 operations.
 __device__ __forceinline__ uint4 q4_expand(uint32_t w) {
-  const uint32_t lo = __builtin_amdgcn_perm(0u, w, 0x0c010c00u);   // bytes 0,1 -> 16-bit lanes
-  const uint32_t hi = __builtin_amdgcn_perm(0u, w, 0x0c030c02u);   // bytes 2,3
-  const uint32_t m = 0x000F000Fu, e = 0x43004300u;
-  return uint4{(lo & m) | e, ((lo >> 4) & m) | e, (hi & m) | e, ((hi >> 4) & m) | e};
+  const uint32_t x0 = w & 0x0F0F0F0Fu, x1 = (w >> 4) & 0x0F0F0F0Fu, e = 0x43434343u;
+  // selector bytes 0-3 pick bytes of the second operand, 4-7 bytes of the first
+  return uint4{__builtin_amdgcn_perm(e, x0, 0x04010400u), __builtin_amdgcn_perm(e, x1, 0x04010400u),
+               __builtin_amdgcn_perm(e, x0, 0x04030402u), __builtin_amdgcn_perm(e, x1, 0x04030402u)};
 }
 
 // the same lane order applied to eight bf16 hidden values
