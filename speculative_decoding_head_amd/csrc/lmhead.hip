@@ -442,9 +442,29 @@ static size_t lmhead_lds_bytes(int wtype, int d, int M) {
   return b + kWaves * 16 * sizeof(RowAcc) + 16;
 }
 
+// Blocks of one launch (a function of the vocabulary rows only, so a row's merge order never
+// depends on the launch size).  A wave takes its tiles TV at a time, so the launch lasts
+// about (passes of its busiest wave) x blocks pass-times of streaming: pick the block count
+// in [lmhead_grid / 2, lmhead_grid] that minimises that product, preferring more blocks on
+// ties.  152,064 rows: 9,504 tiles = 198 blocks x 8 waves x 6 tiles exactly (256 blocks
+// would give some waves 5 tiles and others 4).
+static int lmhead_launch_grid(int n_rows, int tv) {
+  const int tiles = (n_rows + 15) / 16;
+  const int gmax = lmhead_grid(n_rows);   // the workspace holds this many partials per row
+  int best = gmax;
+  long long best_cost = -1;
+  for (int G = gmax; G >= (gmax + 1) / 2; --G) {
+    const long long waves = (long long)G * kWaves;
+    const long long passes = ((tiles + waves - 1) / waves + tv - 1) / tv;
+    const long long cost = passes * G;
+    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = G; }
+  }
+  return best;
+}
+
 template <int WT, bool SAMPLED>
 static hipError_t launch_t(const LmheadLaunch& p, hipStream_t stream) {
-  const int G = lmhead_grid(p.n_rows);
+  const int G = lmhead_launch_grid(p.n_rows, Layout<WT>::q4 ? kTVQ4 : kTV);
   const size_t lds = lmhead_lds_bytes(WT, p.d, p.M);
   auto kern = p.verify ? mtp_verify_logits_kernel<WT, SAMPLED> : mtp_draft_head_kernel<WT, SAMPLED>;
   if (lds > 65536) {
