@@ -47,6 +47,9 @@ using namespace lm;
 #ifndef MTP_LM_U_Q4
 #define MTP_LM_U_Q4 8
 #endif
+#ifndef MTP_LM_TV_Q4_SAMPLED
+#define MTP_LM_TV_Q4_SAMPLED 1
+#endif
 #ifndef MTP_LM_MAX_GRID
 #define MTP_LM_MAX_GRID 256
 #endif
@@ -59,6 +62,15 @@ constexpr int kTV = MTP_LM_TV;       // 16-row vocabulary tiles per wave per pas
 constexpr int kU = MTP_LM_U;         // K steps per prefetch chunk
 constexpr int kTVQ4 = MTP_LM_TV_Q4;  // the same for 4-bit heads, whose K steps carry a
 constexpr int kUQ4 = MTP_LM_U_Q4;    // quarter of the bytes
+// 4-bit heads under sampling keep the Gumbel state live through the K loop: one tile per
+// pass keeps them out of scratch (two spilled 108-156 bytes per lane and ran 9-11% slower)
+constexpr int kTVQ4S = MTP_LM_TV_Q4_SAMPLED;
+
+// tiles per wave pass of a launch
+template <int WT, bool SAMPLED>
+constexpr int tiles_per_pass() {
+  return Layout<WT>::q4 ? (SAMPLED ? kTVQ4S : kTVQ4) : kTV;
+}
 constexpr int kMaxGrid = MTP_LM_MAX_GRID;
 
 template <int WT, bool SAMPLED, bool VERIFY>
@@ -69,7 +81,7 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   const int xi = lane & 15, g = lane >> 4;
   const int M = p.M, d = p.d;
   using L = Layout<WT>;
-  constexpr int TV = L::q4 ? kTVQ4 : kTV;
+  constexpr int TV = tiles_per_pass<WT, SAMPLED>();
   constexpr int U = L::q4 ? kUQ4 : kU;
   static_assert(!L::q4 || U % 8 == 0, "4-bit chunks cover whole octets of groups (one scale vector each)");
   const int nsteps = L::f32 ? d / 16 : d / 32;
@@ -464,7 +476,7 @@ static int lmhead_launch_grid(int n_rows, int tv) {
 
 template <int WT, bool SAMPLED>
 static hipError_t launch_t(const LmheadLaunch& p, hipStream_t stream) {
-  const int G = lmhead_launch_grid(p.n_rows, Layout<WT>::q4 ? kTVQ4 : kTV);
+  const int G = lmhead_launch_grid(p.n_rows, tiles_per_pass<WT, SAMPLED>());
   const size_t lds = lmhead_lds_bytes(WT, p.d, p.M);
   auto kern = p.verify ? mtp_verify_logits_kernel<WT, SAMPLED> : mtp_draft_head_kernel<WT, SAMPLED>;
   if (lds > 65536) {
