@@ -11,13 +11,18 @@
 // comment "Review"); EOS inside the block ends it with nothing kept beyond EOS (same
 // issue, "Implementation").
 //
-// Grid (B, S): every block walks the request's acceptance chain (at most 7 rows of
-// per-row statistics), then, if the request stopped at a rejection with T > 0, scores
-// its 1/S slice of the vocabulary for the residual draw: ln r(x) + Gumbel(x) with
-// ln r = ln p + log1p(-exp(ln q - ln p)) where p > q.  Each block writes its best
-// (score, id) and whether it saw residual mass; the last of the S blocks to finish
-// (atomic ticket per request) merges the slices in order and writes the request's
-// tokens, counts and flags.  At T = 0, S = 1 and no workspace is used.
+// Grid (B, S), one wave per 64 threads.  Every wave evaluates the request's acceptance
+// chain in parallel, lane i for draft row i and lane k for the bonus row, and finds the
+// first row that stops the block with a ballot: all rows' statistics (and under the ratio
+// rule their drafted-id logits and acceptance draws) are fetched at once, not one
+// dependent round trip per row.  If the request stopped at a rejection with T > 0, each
+// block then scores its 1/S slice of the vocabulary (about 1,024 ids, one pass per thread)
+// for the residual draw: ln r(x) + Gumbel(x) with ln r = ln p + log1p(-exp(ln q - ln p))
+// where p > q.  Each block writes its best (score, id) and whether it saw residual mass;
+// the last of the S blocks to finish (atomic ticket per request) loads all slice results
+// at once and reduces them (the comparison is a total order: higher score, then lower id,
+// so the result does not depend on the reduction order) and writes the request's tokens,
+// counts and flags.  At T = 0, S = 1 and no workspace is used.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,8 +30,8 @@ namespace mtp {
 
 namespace {
 
-constexpr int kSliceElems = 4096;
-constexpr int kMaxSlices = 64;
+constexpr int kSliceElems = 1024;
+constexpr int kMaxSlices = 256;   // 4 slice results per lane of one wave in the final merge
 
 struct SlicePartial {
   float score;
@@ -42,6 +47,10 @@ struct Chain {
   int kind;      // StopKind
   int last;      // token after the accepted drafts (kInvalidRow: none)
   uint32_t flags;
+  // statistics of the verify row and draft row at index a
+  uint32_t vflags, dflags;
+  float vlse, dlse;
+  int vsample, vargmax;
 };
 
 // draft row of vocabulary id x (-1: outside the draft vocabulary)
@@ -59,29 +68,32 @@ __device__ __forceinline__ float draft_logq(const AcceptLaunch& p, int b, int i,
   return z * inv_t - ds.lse;
 }
 
-__device__ Chain walk_chain(const AcceptLaunch& p, int b, float inv_t) {
-  Chain c{p.k, kAllAccepted, -1, 0u};
+// The acceptance chain of request b, evaluated by one wave: lane i < k takes draft row i,
+// lane k the bonus row.  A row stops the block if its target row is unusable, its draft is
+// rejected or its accepted draft is EOS; the bonus row always stops it.  Flags come from
+// every row before the stopping one and from the stopping row itself unless its target row
+// is unusable (the block ends before that row).  Every lane returns the same chain.
+__device__ Chain walk_chain(const AcceptLaunch& p, int b, float inv_t, int lane) {
   const bool sampled = p.temperature > 0.0f;
   const int K1 = p.k + 1;
-  for (int i = 0; i < p.k; ++i) {
-    const mtp_row_stats vs = p.vstats[(size_t)b * K1 + i];
-    if (vs.flags & MTP_ROW_INVALID) {
-      c.a = i;
-      c.kind = kInvalidRow;
-      return c;
-    }
-    if (vs.flags & MTP_ROW_NONFINITE) c.flags |= MTP_ACC_NONFINITE_TARGET;
-    const mtp_row_stats ds = p.dstats[(size_t)b * p.k_max + i];
-    if (ds.flags & MTP_ROW_NONFINITE) c.flags |= MTP_ACC_NONFINITE_DRAFT;
-    const int t = p.drafts[(size_t)b * p.k_max + i];
+  const int i = lane;
+  mtp_row_stats vs{}, ds{};
+  int t = -1;
+  if (i < K1) vs = p.vstats[(size_t)b * K1 + i];
+  if (i < p.k) {
+    ds = p.dstats[(size_t)b * p.k_max + i];
+    t = p.drafts[(size_t)b * p.k_max + i];
+  }
+  const bool invalid = i < K1 && (vs.flags & MTP_ROW_INVALID);
+  uint32_t rf = (i < K1 && (vs.flags & MTP_ROW_NONFINITE)) ? MTP_ACC_NONFINITE_TARGET : 0u;
+  bool ok = false, eos = false;
+  if (i < p.k) {
+    if (ds.flags & MTP_ROW_NONFINITE) rf |= MTP_ACC_NONFINITE_DRAFT;
     const bool t_ok = t >= 0 && t < p.vocab;
-    if (!t_ok) c.flags |= MTP_ACC_DRAFT_INVALID;
-    bool ok;
+    if (!t_ok) rf |= MTP_ACC_DRAFT_INVALID;
     if (!sampled || p.exact) {
       ok = t_ok && t == (sampled ? vs.sample : vs.argmax);
-    } else if (!t_ok) {
-      ok = false;
-    } else {
+    } else if (t_ok) {
       const float zt = sanitize(p.vlogits[((size_t)b * K1 + i) * p.vocab + t], vs.flags);
       const float lp = zt * inv_t - vs.lse;
       const float lq = draft_logq(p, b, i, t, inv_t, ds);
@@ -90,26 +102,38 @@ __device__ Chain walk_chain(const AcceptLaunch& p, int b, float inv_t) {
       const float lu = logf(uniform_accept(w));
       ok = lp > kNegInf && (lu + lq) <= lp;
     }
-    if (!ok) {
-      c.a = i;
-      c.kind = kRejected;
-      return c;
-    }
-    if (p.eos >= 0 && t == p.eos) {
-      c.a = i;
-      c.kind = kEosDraft;
-      c.last = p.eos;
-      return c;
-    }
+    eos = p.eos >= 0 && t == p.eos;
   }
-  const mtp_row_stats vk = p.vstats[(size_t)b * K1 + p.k];
-  if (vk.flags & MTP_ROW_INVALID) {
-    c.a = p.k;
+  const bool stop = i == p.k || (i < p.k && (invalid || !ok || eos));
+  const int s = __ffsll((unsigned long long)__ballot(stop)) - 1;   // lane k always stops: k <= 7
+  uint32_t fl = (i < s || (i == s && !invalid)) ? rf : 0u;
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) fl |= __shfl_xor(fl, m);   // rows 0..7 live in lanes 0..7
+
+  Chain c;
+  c.a = s;
+  c.flags = __shfl(fl, 0);
+  const bool inv_s = __shfl(invalid ? 1 : 0, s) != 0;
+  const bool ok_s = __shfl(ok ? 1 : 0, s) != 0;
+  c.vflags = __shfl(vs.flags, s);
+  c.vlse = __shfl(vs.lse, s);
+  c.vsample = __shfl(vs.sample, s);
+  c.vargmax = __shfl(vs.argmax, s);
+  c.dflags = __shfl(ds.flags, s);
+  c.dlse = __shfl(ds.lse, s);
+  if (inv_s) {
     c.kind = kInvalidRow;
-    return c;
+    c.last = -1;
+  } else if (s == p.k) {
+    c.kind = kAllAccepted;
+    c.last = sampled ? c.vsample : c.vargmax;
+  } else if (!ok_s) {
+    c.kind = kRejected;
+    c.last = -1;
+  } else {
+    c.kind = kEosDraft;
+    c.last = p.eos;
   }
-  if (vk.flags & MTP_ROW_NONFINITE) c.flags |= MTP_ACC_NONFINITE_TARGET;
-  c.last = sampled ? vk.sample : vk.argmax;
   return c;
 }
 
@@ -125,7 +149,7 @@ __global__ __launch_bounds__(kAcceptThreads) void mtp_accept_sample_kernel(Accep
   const float inv_t = sampled ? 1.0f / p.temperature : 1.0f;
   const int K1 = p.k + 1;
 
-  Chain c = walk_chain(p, b, inv_t);
+  Chain c = walk_chain(p, b, inv_t, lane);
   const bool resample = sampled && !p.exact && c.kind == kRejected;
 
   // ---- residual slice: best ln r(x) + Gumbel(x) over x in this block's range ------
@@ -134,12 +158,10 @@ __global__ __launch_bounds__(kAcceptThreads) void mtp_accept_sample_kernel(Accep
   int mass = 0;
   if (resample) {
     const int i = c.a;
-    const mtp_row_stats vs = p.vstats[(size_t)b * K1 + i];
-    const mtp_row_stats ds = p.dstats[(size_t)b * p.k_max + i];
     const float* zrow = p.vlogits + ((size_t)b * K1 + i) * p.vocab;
     const float* qrow = p.dlogits + ((size_t)b * p.k_max + i) * p.n_draft;
-    const bool q_valid = !(ds.flags & MTP_ROW_INVALID);
-    const int per = (p.vocab + S - 1) / S;
+    const bool q_valid = !(c.dflags & MTP_ROW_INVALID);
+    const int per = ((p.vocab + S - 1) / S + 3) & ~3;   // slices start on groups of 4 ids
     const int x0 = slice * per, x1 = min(p.vocab, x0 + per);
     const uint32_t prow = (kStreamResample << 8) | (uint32_t)i;
     const uint32_t preq = p.request_base + (uint32_t)b;
@@ -150,9 +172,9 @@ __global__ __launch_bounds__(kAcceptThreads) void mtp_accept_sample_kernel(Accep
       for (int e = 0; e < 4; ++e) {
         const int x = xg + e;
         if (x < x0 || x >= x1) continue;
-        const float lp = sanitize(zrow[x], vs.flags) * inv_t - vs.lse;
+        const float lp = sanitize(zrow[x], c.vflags) * inv_t - c.vlse;
         const int dr = q_valid ? draft_row(p, x) : -1;
-        const float lq = (dr >= 0 && dr < p.n_draft) ? sanitize(qrow[dr], ds.flags) * inv_t - ds.lse : kNegInf;
+        const float lq = (dr >= 0 && dr < p.n_draft) ? sanitize(qrow[dr], c.dflags) * inv_t - c.dlse : kNegInf;
         if (lp > lq) {
           const float lr = lp + log1pf(-__expf(lq - lp));
           if (lr > kNegInf) {
@@ -192,17 +214,29 @@ __global__ __launch_bounds__(kAcceptThreads) void mtp_accept_sample_kernel(Accep
       s_last = (take_ticket(&counters[b]) == (unsigned)S - 1);
     }
     __syncthreads();
-    if (!s_last) return;
-    if (tid != 0) return;
-    float bs = kNegInf;
-    int bi = kNoIndex, bm = 0;
-    for (int sl = 0; sl < S; ++sl) {
-      const SlicePartial q = load_coherent_obj(&part[(size_t)b * S + sl]);
-      if (better(q.score, q.idx, bs, bi)) { bs = q.score; bi = q.idx; }
-      bm |= q.has_mass;
+    if (!s_last || wave != 0) return;
+    // wave 0: every slice result is loaded at once (up to 4 per lane), then reduced
+    SlicePartial q[kMaxSlices / 64];
+#pragma unroll
+    for (int u = 0; u < kMaxSlices / 64; ++u) {
+      const int sl = lane + 64 * u;
+      q[u] = sl < S ? load_coherent_obj(&part[(size_t)b * S + sl]) : SlicePartial{kNegInf, kNoIndex, 0, 0};
     }
+    best = kNegInf; best_idx = kNoIndex; mass = 0;
+#pragma unroll
+    for (int u = 0; u < kMaxSlices / 64; ++u) {
+      if (better(q[u].score, q[u].idx, best, best_idx)) { best = q[u].score; best_idx = q[u].idx; }
+      mass |= q[u].has_mass;
+    }
+    for (int m = 1; m < 64; m <<= 1) {
+      const float ob = __shfl_xor(best, m);
+      const int oi = __shfl_xor(best_idx, m);
+      const int om = __shfl_xor(mass, m);
+      if (better(ob, oi, best, best_idx)) { best = ob; best_idx = oi; }
+      mass |= om;
+    }
+    if (lane != 0) return;
     store_coherent(&counters[b], 0u);
-    best = bs; best_idx = bi; mass = bm;
   } else {
     if (tid != 0) return;
     best = s_score[0]; best_idx = s_idx[0]; mass = s_mass[0];
@@ -214,16 +248,15 @@ __global__ __launch_bounds__(kAcceptThreads) void mtp_accept_sample_kernel(Accep
 
   // ---- one thread writes the request's result ------------------------------------
   if (c.kind == kRejected) {
-    const mtp_row_stats vs = p.vstats[(size_t)b * K1 + c.a];
     if (!sampled) {
-      c.last = vs.argmax;
+      c.last = c.vargmax;
     } else if (p.exact) {
-      c.last = vs.sample;   // the trunk's own sample at this position
+      c.last = c.vsample;   // the trunk's own sample at this position
     } else if (mass) {
       c.last = best_idx;
     } else {
       c.flags |= MTP_ACC_RESID_FALLBACK;
-      c.last = vs.sample;   // argmax(z/T + Gumbel) on the same stream-2 draws = a draw from p
+      c.last = c.vsample;   // argmax(z/T + Gumbel) on the same stream-2 draws = a draw from p
     }
   }
   if (c.kind == kAllAccepted) c.flags |= MTP_ACC_ALL_ACCEPTED;
