@@ -73,6 +73,12 @@ constexpr int tiles_per_pass() {
 }
 constexpr int kMaxGrid = MTP_LM_MAX_GRID;
 
+// Quad broadcast on the DPP network: every lane of each group of 4 reads lane R's value.
+template <int R>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, R * 0x55, 0xF, 0xF, false);
+}
+
 template <int WT, bool SAMPLED, bool VERIFY>
 __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   static_assert(sizeof(RowAcc) == 48, "partials are three 16-byte vectors");
@@ -274,6 +280,17 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
     pcyc[r] = (bypos && rvalid[r]) ? (uint32_t)(p.positions[b] + i) : p.cycle;
     tok[r] = (VERIFY && rvalid[r] && i < p.k) ? p.drafts[(size_t)b * p.k_max + i] : -1;
   }
+  // Gumbel draws of ids x = 4m..4m+3 for one hidden row are the four words of one Philox
+  // block, and lanes 4m..4m+3 of a 16-lane row hold those ids for the same four hidden
+  // rows: lane 4m+e computes the block of row 4g+e and the quad exchanges the words (the
+  // same draws at a quarter of the Philox work).  Used when the ids are the rows (verify,
+  // or a draft head without an id list) and there is more than one hidden row.
+  const bool quad_draws = SAMPLED && (VERIFY || p.ids == nullptr) && M > 1;
+  const int qe = xi & 3;
+  uint32_t prow_q = prow[0], preq_q = preq[0], pcyc_q = pcyc[0];
+#pragma unroll
+  for (int r = 1; r < 4; ++r)
+    if (qe == r) { prow_q = prow[r]; preq_q = preq[r]; pcyc_q = pcyc[r]; }
 
   RowAcc acc[4];
 #pragma unroll
@@ -299,7 +316,23 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
 #pragma unroll
     for (int t = 0; t < TV; ++t) {
       const int x = (tb + t) * 16 + xi;
-      if ((tb + t) >= t_end || x >= p.n_rows) continue;
+      if ((tb + t) >= t_end) continue;   // wave-uniform: every lane takes part in the exchange
+      float gq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (SAMPLED && quad_draws) {
+        const u32x4 wd = philox4x32_10(u32x4{(uint32_t)x >> 2, prow_q, preq_q, pcyc_q}, p.key0, p.key1);
+        auto word_of = [&](auto rc) {   // word qe of row rc's block, from lane rc of the quad
+          constexpr int R = decltype(rc)::value;
+          const uint32_t w0 = quad_bcast<R>(wd.x), w1 = quad_bcast<R>(wd.y);
+          const uint32_t w2 = quad_bcast<R>(wd.z), w3 = quad_bcast<R>(wd.w);
+          return qe == 0 ? w0 : (qe == 1 ? w1 : (qe == 2 ? w2 : w3));
+        };
+        const uint32_t wq[4] = {word_of(std::integral_constant<int, 0>{}), word_of(std::integral_constant<int, 1>{}),
+                                word_of(std::integral_constant<int, 2>{}), word_of(std::integral_constant<int, 3>{})};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (rvalid[r]) gq[r] = gumbel_from_word(wq[r]);
+      }
+      if (x >= p.n_rows) continue;
       // a draft head gathered from a set of ids: its row x stands for vocabulary id
       // ids[x]; ids and draws refer to the vocabulary, the stored logits to the row
       const int xv = (!VERIFY && p.ids) ? p.ids[x] : x;
@@ -308,8 +341,8 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
         if (!rvalid[r]) continue;
         const int j = 4 * g + r;
         const float z = c[t][r];
-        float gn = 0.0f;
-        if (SAMPLED) {
+        float gn = gq[r];
+        if (SAMPLED && !quad_draws) {
           const u32x4 wd = philox4x32_10(u32x4{(uint32_t)xv >> 2, prow[r], preq[r], pcyc[r]}, p.key0, p.key1);
           const int sel = xv & 3;
           gn = gumbel_from_word(sel == 0 ? wd.x : (sel == 1 ? wd.y : (sel == 2 ? wd.z : wd.w)));
