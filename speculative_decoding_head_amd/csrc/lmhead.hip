@@ -79,8 +79,12 @@ __device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, R * 0x55, 0xF, 0xF, false);
 }
 
-template <int WT, bool SAMPLED, bool VERIFY>
+// RL: accumulator rows a lane can hold live (row 4g + r exists only if r < M).  4-bit heads
+// apply each group's scale and min per accumulator row on the VALU, so a launch of one
+// hidden row (the draft head of one request) skips the three rows no lane holds.
+template <int WT, bool SAMPLED, bool VERIFY, int RL>
 __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
+  static_assert(RL == 1 || RL == 4, "one live row or all four");
   static_assert(sizeof(RowAcc) == 48, "partials are three 16-byte vectors");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -219,7 +223,7 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
           const float mv = bf16_to_f32((uint16_t)((u & 1) ? (mw >> 16) : (mw & 0xFFFFu)));
           const float off = mv - 128.0f * sv;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) c[t][r] = fmaf(off, hs[r], fmaf(sv, D[r], c[t][r]));
+          for (int r = 0; r < RL; ++r) c[t][r] = fmaf(off, hs[r], fmaf(sv, D[r], c[t][r]));
         }
       }
     }
@@ -458,16 +462,16 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
 
 }  // namespace
 
-template <int WT, bool SAMPLED>
+template <int WT, bool SAMPLED, int RL>
 __global__ __launch_bounds__(kLmheadThreads) __attribute__((amdgpu_waves_per_eu(MTP_LM_WAVES_PER_EU)))
 void mtp_draft_head_kernel(LmheadLaunch p) {
-  lmhead_body<WT, SAMPLED, false>(p);
+  lmhead_body<WT, SAMPLED, false, RL>(p);
 }
 
 template <int WT, bool SAMPLED>
 __global__ __launch_bounds__(kLmheadThreads) __attribute__((amdgpu_waves_per_eu(MTP_LM_WAVES_PER_EU)))
 void mtp_verify_logits_kernel(LmheadLaunch p) {
-  lmhead_body<WT, SAMPLED, true>(p);
+  lmhead_body<WT, SAMPLED, true, 4>(p);
 }
 
 int lmhead_grid(int n_rows) {
@@ -511,7 +515,10 @@ template <int WT, bool SAMPLED>
 static hipError_t launch_t(const LmheadLaunch& p, hipStream_t stream) {
   const int G = lmhead_launch_grid(p.n_rows, tiles_per_pass<WT, SAMPLED>());
   const size_t lds = lmhead_lds_bytes(WT, p.d, p.M);
-  auto kern = p.verify ? mtp_verify_logits_kernel<WT, SAMPLED> : mtp_draft_head_kernel<WT, SAMPLED>;
+  // the one-row specialisation only changes 4-bit heads' code
+  auto kern = p.verify ? mtp_verify_logits_kernel<WT, SAMPLED>
+                       : ((Layout<WT>::q4 && p.M == 1) ? mtp_draft_head_kernel<WT, SAMPLED, 1>
+                                                       : mtp_draft_head_kernel<WT, SAMPLED, 4>);
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
