@@ -28,6 +28,7 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0   # dense MFMA, bf16
 METRIC = "verify cycles/s (k=7, V=152,064, d=2560 bf16) + achieved HBM GB/s vs peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+UTIL_FILE = os.path.join(ROOT, "profiles", "mfma_valu.json")
 # sources the LM-head kernels are compiled from: counters taken on other sources are stale
 KERNEL_SRCS = [os.path.join(ROOT, "speculative_decoding_head_amd", "csrc", f)
                for f in ("lmhead.hip", "lmhead_wide.hip", "lmhead_common.hpp", "common.hpp", "kernels.hpp")]
@@ -61,6 +62,9 @@ def parse():
                     help="keep the head row-major instead of repacking it once into the tiled layout")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (the HBM counter reference)")
+    ap.add_argument("--summarize-utilisation", nargs=2, action="append", metavar=("WORKLOAD", "CSV"),
+                    help="turn a rocprofv3 --pmc MfmaUtil VALUBusy MfmaFlopsBF16 CSV of a run of WORKLOAD into "
+                         "profiles/mfma_valu.json (repeat once per workload)")
     ap.add_argument("--summarize-counters", nargs=3, action="append", metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV"),
                     help="turn the rocprofv3 --pmc CSVs (FETCH_SIZE, WRITE_SIZE) of a run of WORKLOAD into "
                          "profiles/traffic.json (repeat once per workload)")
@@ -117,6 +121,43 @@ def summarize_counters(runs) -> None:
     print(json.dumps(out, indent=1))
 
 
+def summarize_utilisation(runs) -> None:
+    """Per-kernel MFMA and VALU busy percentages and MFMA bf16 flops per launch (medians over
+    the run's launches) from rocprofv3 counter CSVs, per workload."""
+    import csv
+    from collections import defaultdict
+
+    out = {"source_digest": source_digest(), "workloads": {}}
+    for workload, path in runs:
+        per = defaultdict(lambda: defaultdict(list))
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                name = row["Kernel_Name"]
+                short = next((key for key in KERNEL_KEYS if key + "<" in name or key + "(" in name), None)
+                if short is not None:
+                    per[short][row["Counter_Name"]].append(float(row["Counter_Value"]))
+        out["workloads"][workload] = {
+            k: {"mfma_busy_pct": round(float(np.median(v["MfmaUtil"])), 2),
+                "valu_busy_pct": round(float(np.median(v["VALUBusy"])), 2),
+                "mfma_bf16_flops": int(np.median(v["MfmaFlopsBF16"])),
+                "launches": len(v["MfmaUtil"])}
+            for k, v in per.items() if "MfmaUtil" in v}
+    with open(UTIL_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def load_utilisation(workload: str, kernel: str):
+    """Counter-measured MFMA/VALU busy of a kernel, if taken on this source."""
+    try:
+        t = json.load(open(UTIL_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_digest") != source_digest():
+        return None
+    return t.get("workloads", {}).get(workload, {}).get(kernel)
+
+
 def source_digest() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SRCS:
@@ -141,8 +182,11 @@ def load_traffic(workload: str, kernel: str):
 
 def main():
     args = parse()
-    if args.summarize_counters:
-        summarize_counters(args.summarize_counters)
+    if args.summarize_counters or args.summarize_utilisation:
+        if args.summarize_counters:
+            summarize_counters(args.summarize_counters)
+        if args.summarize_utilisation:
+            summarize_utilisation(args.summarize_utilisation)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -288,7 +332,9 @@ def main():
             # the verify product runs on MFMA: its algorithmic rate against the dense bf16 peak
             r["mfma"] = {"algorithmic_flops_per_launch": int(flops),
                          "achieved_TFLOPs": round(flops / avg_s / 1e12, 1),
-                         "frac_of_dense_bf16_peak": round(flops / avg_s / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                         "frac_of_dense_bf16_peak": round(flops / avg_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         # rocprofv3 MfmaUtil / VALUBusy of the same kernel (profiles/mfma_valu.json)
+                         "counters": load_utilisation(args.workload, kernel)}
         return r
 
     draft_kernel = "mtp_draft_head_kernel"
