@@ -57,7 +57,11 @@ using namespace lm;
 #define MTP_LM_WAVES_PER_EU 1
 #endif
 
-constexpr int kWaves = kLmheadThreads / 64;
+#ifndef MTP_LM_WAVES
+#define MTP_LM_WAVES 8
+#endif
+constexpr int kWaves = MTP_LM_WAVES;   // waves per block
+constexpr int kThreads = 64 * kWaves;
 constexpr int kTV = MTP_LM_TV;       // 16-row vocabulary tiles per wave per pass
 constexpr int kU = MTP_LM_U;         // K steps per prefetch chunk
 constexpr int kTVQ4 = MTP_LM_TV_Q4;  // the same for 4-bit heads, whose K steps carry a
@@ -245,22 +249,22 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
     }
     return v;
   };
-  constexpr int kPreFrags = 10;
+  constexpr int kPreFrags = 80 / kWaves;   // d = 2560 at 16 rows: 5,120 fragments per block
   uint4 hv[kPreFrags];
 #pragma unroll
   for (int q = 0; q < kPreFrags; ++q)
-    if (tid + q * kLmheadThreads < nfrag) hv[q] = hfrag(tid + q * kLmheadThreads);
+    if (tid + q * kThreads < nfrag) hv[q] = hfrag(tid + q * kThreads);
   Chunk A, B;
   uint32_t roff_cur[TV], roff_nxt[TV];
   row_offsets(t_begin, roff_cur);
   load(A, roff_cur, 0);
 #pragma unroll
   for (int q = 0; q < kPreFrags; ++q)
-    if (tid + q * kLmheadThreads < nfrag) frag[tid + q * kLmheadThreads] = hv[q];
-  for (int f = tid + kPreFrags * kLmheadThreads; f < nfrag; f += kLmheadThreads) frag[f] = hfrag(f);
+    if (tid + q * kThreads < nfrag) frag[tid + q * kThreads] = hv[q];
+  for (int f = tid + kPreFrags * kThreads; f < nfrag; f += kThreads) frag[f] = hfrag(f);
   if (L::q4) {
     // per 32-value group and hidden row: sum of the hidden values
-    for (int e = tid; e < nsteps * 16; e += kLmheadThreads) {
+    for (int e = tid; e < nsteps * 16; e += kThreads) {
       const int s = e >> 4, i = e & 15;
       htab[e] = i < M ? group_sum32(static_cast<const uint16_t*>(p.hidden) + (size_t)i * d + 32 * s) : 0.0f;
     }
@@ -394,20 +398,27 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   __syncthreads();
   if (!*last_flag) return;
 
-  // ---- last block: wave w merges rows w and w + 8 (M <= 16): 4 partials per lane in
-  //      block order, then a butterfly over the 64 lanes (DPP inside rows of 16, exchanges
-  //      across them).  One fixed tree for every row and every M, so a row's statistics do
-  //      not depend on the launch size.  The two rows' chains are interleaved step by step,
-  //      and every partial load (and the drafted-id logit) goes out before the first merge:
-  //      these loads bypass the caches and each round trip is long.
-  static_assert(kLmheadMaxRows <= 2 * kWaves && kMaxGrid <= 4 * 64, "two rows per wave, 4 partials per lane");
+  // ---- last block: wave w merges rows w, w + kWaves, ... (M <= 16): 4 partials per lane
+  //      in block order, then a butterfly over the 64 lanes (DPP inside rows of 16,
+  //      exchanges across them).  One fixed tree for every row and every M, so a row's
+  //      statistics do not depend on the launch size.  The rows' chains are interleaved
+  //      step by step, and every partial load (and the drafted-id logit) goes out before the
+  //      first merge: these loads bypass the caches and each round trip is long.
+  constexpr int RPW = kLmheadMaxRows / kWaves;   // rows per wave
+  static_assert(RPW * kWaves == kLmheadMaxRows && kMaxGrid <= 4 * 64, "whole rows per wave, 4 partials per lane");
   {
     constexpr int NP = kMaxGrid / 64;
-    const int jr[2] = {wave, wave + kWaves};
-    RowAcc part[2][NP];
-    uint32_t zbits[2];
+    int jr[RPW];
+    bool live[RPW];   // wave-uniform: a chain runs only when it has a row (chain 0 always)
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < RPW; ++r) {
+      jr[r] = wave + kWaves * r;
+      live[r] = r == 0 || jr[r] < M;
+    }
+    RowAcc part[RPW][NP];
+    uint32_t zbits[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
 #pragma unroll
       for (int q = 0; q < NP; ++q) {
         const int blk = lane + 64 * q;
@@ -416,22 +427,23 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
       }
       zbits[r] = (VERIFY && jr[r] < M) ? load_coherent(reinterpret_cast<const uint32_t*>(ztok) + jr[r]) : 0u;
     }
-    RowAcc a[2] = {part[0][0], part[1][0]};
-    const bool two = jr[1] < M;   // wave-uniform: the second chain only when it has a row
+    RowAcc a[RPW];
 #pragma unroll
-    for (int q = 1; q < NP; ++q) {
-      rowacc_merge(a[0], part[0][q]);
-      if (two) rowacc_merge(a[1], part[1][q]);
-    }
-    // one butterfly step on both chains; the exchange reads a lane's partner before
-    // either merge writes
+    for (int r = 0; r < RPW; ++r) a[r] = part[r][0];
+#pragma unroll
+    for (int q = 1; q < NP; ++q)
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        if (live[r]) rowacc_merge(a[r], part[r][q]);
+    // one butterfly step on every chain; the exchange reads a lane's partner before the
+    // merge writes
     auto bfly = [&](auto xchg) {
-      const RowAcc o0 = xchg(a[0]);
-      if (two) {
-        const RowAcc o1 = xchg(a[1]);
-        rowacc_merge(a[1], o1);
-      }
-      rowacc_merge(a[0], o0);
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        if (live[r]) {
+          const RowAcc o = xchg(a[r]);
+          rowacc_merge(a[r], o);
+        }
     };
     bfly([](const RowAcc& x) { return rowacc_xor16<1>(x); });
     bfly([](const RowAcc& x) { return rowacc_xor16<2>(x); });
@@ -440,7 +452,7 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
     bfly([](const RowAcc& x) { return rowacc_shfl_xor(x, 16); });
     bfly([](const RowAcc& x) { return rowacc_shfl_xor(x, 32); });
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < RPW; ++r) {
       const int j = jr[r];
       if (j >= M || lane != 0) continue;
       mtp_row_stats st = finalize_row(a[r], SAMPLED);
@@ -463,20 +475,20 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
 }  // namespace
 
 template <int WT, bool SAMPLED, int RL>
-__global__ __launch_bounds__(kLmheadThreads) __attribute__((amdgpu_waves_per_eu(MTP_LM_WAVES_PER_EU)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MTP_LM_WAVES_PER_EU)))
 void mtp_draft_head_kernel(LmheadLaunch p) {
   lmhead_body<WT, SAMPLED, false, RL>(p);
 }
 
 template <int WT, bool SAMPLED>
-__global__ __launch_bounds__(kLmheadThreads) __attribute__((amdgpu_waves_per_eu(MTP_LM_WAVES_PER_EU)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MTP_LM_WAVES_PER_EU)))
 void mtp_verify_logits_kernel(LmheadLaunch p) {
   lmhead_body<WT, SAMPLED, true, 4>(p);
 }
 
 int lmhead_grid(int n_rows) {
   const int tiles = (n_rows + 15) / 16;
-  const int g = (tiles + 2 * kWaves - 1) / (2 * kWaves);
+  const int g = (tiles + 15) / 16;   // the workspace's partials per row: one per 16 tiles, at most 256
   return g < 1 ? 1 : (g > kMaxGrid ? kMaxGrid : g);
 }
 
@@ -516,15 +528,15 @@ static hipError_t launch_t(const LmheadLaunch& p, hipStream_t stream) {
   const int G = lmhead_launch_grid(p.n_rows, tiles_per_pass<WT, SAMPLED>());
   const size_t lds = lmhead_lds_bytes(WT, p.d, p.M);
   // the one-row specialisation only changes 4-bit heads' code
-  auto kern = p.verify ? mtp_verify_logits_kernel<WT, SAMPLED>
-                       : ((Layout<WT>::q4 && p.M == 1) ? mtp_draft_head_kernel<WT, SAMPLED, 1>
-                                                       : mtp_draft_head_kernel<WT, SAMPLED, 4>);
+  auto kern = p.verify ? mtp_verify_logits_kernel<WT, SAMPLED> : mtp_draft_head_kernel<WT, SAMPLED, 4>;
+  if constexpr (Layout<WT>::q4)
+    if (!p.verify && p.M == 1) kern = mtp_draft_head_kernel<WT, SAMPLED, 1>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3(G), dim3(kLmheadThreads), lds, stream, p);
+  hipLaunchKernelGGL(kern, dim3(G), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
