@@ -61,13 +61,12 @@ __global__ __launch_bounds__(kCommitThreads) void mtp_commit_state_kernel(Commit
     const int lo = min(len + a + 1, p.max_rows), hi = min(len + p.k + 1, p.max_rows);
     const size_t row_vecs = p.kv_row_bytes / 16;
     const size_t per_plane = (size_t)(hi > lo ? hi - lo : 0) * row_vecs;   // vectors per (layer, K|V)
-    const size_t total = per_plane * 2 * p.n_layers;
     unsigned char* base = static_cast<unsigned char*>(p.kv) +
                           (size_t)b * p.n_layers * 2 * p.max_rows * p.kv_row_bytes;
-    for (size_t e = threadIdx.x; e < total; e += kCommitThreads) {
-      const size_t plane = e / per_plane, off = e % per_plane;
-      u32x4* dst = reinterpret_cast<u32x4*>(base + (plane * p.max_rows + lo) * p.kv_row_bytes) + off;
-      *dst = u32x4{0u, 0u, 0u, 0u};
+    // the rejected rows of one plane are contiguous: one plane after the other, no division
+    for (int plane = 0; plane < 2 * p.n_layers; ++plane) {
+      u32x4* dst = reinterpret_cast<u32x4*>(base + ((size_t)plane * p.max_rows + lo) * p.kv_row_bytes);
+      for (size_t off = threadIdx.x; off < per_plane; off += kCommitThreads) dst[off] = u32x4{0u, 0u, 0u, 0u};
     }
   }
   __syncthreads();
