@@ -129,6 +129,31 @@ def test_planted_depths_and_eos(wtype, T):
         assert len(seen) >= 6
 
 
+@pytest.mark.parametrize("V", [2050, 5003])
+def test_residual_draw_over_several_slices(V):
+    """Ratio acceptance at T = 1 over a vocabulary that is not a multiple of 4 and spans several
+    of the accept kernel's residual slices (2050: 3 slices of 684 ids; 5003: 5 slices, the
+    last one short): planted rejections at every depth, tokens, counts and flags against the
+    oracle."""
+    d, nd, k, B = 256, 1500, 7, 3
+    rng = np.random.default_rng(V)
+    head = synth.make_head(rng, V, d, "bf16", keep_source=True)
+    W = O.head_weights_f64(head)
+    gc = GpuCycle(dev_head(head), nd, B, k, 1.0, seed=99, eos=-1)
+    stats = dict(flagged=0, excluded=0)
+    for cyc in range(6):
+        h_v, h_d = synth.make_hidden(rng, B, k, d)
+        depths = [(cyc + 3 * b) % (k + 1) for b in range(B)]
+        targets = rng.integers(3, nd, size=(B, k + 1))
+        synth.plant_rows(head, h_v, h_d, depths, targets, (targets + 11) % nd, margin=12.0)
+        hv, hd = synth.encode_hidden(h_v, "bf16"), synth.encode_hidden(h_d, "bf16")
+        o = O.cycle(W, nd, O.hidden_f64(hd, "bf16"), O.hidden_f64(hv, "bf16"), 1.0, 99, cyc, -1, 2e-2)
+        g = gc.run(dev_hidden(hd), dev_hidden(hv), cycle=cyc)
+        r = check_cycle(g, o, 1.0, 2e-2, tag=f"V{V} cycle {cyc}")
+        stats = {key: stats[key] + r[key] for key in stats}
+    print("near-tie decisions flagged:", stats)
+
+
 def _nonfinite_head(V, d):
     rng = np.random.default_rng(3)
     w = (rng.standard_normal((V, d)) * 0.02).astype(np.float32)
