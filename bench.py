@@ -370,6 +370,10 @@ def main():
         "stages_us": {"draft_head_avg": round(d_avg * 1e6, 2), "verify_avg": round(v_avg * 1e6, 2),
                       "accept_avg": round(float(np.mean(accept_ms)) * 1e3, 2),
                       "commit_avg": round(float(np.mean(commit_ms)) * 1e3, 2)},
+        # spread of the same event samples: 10th and 90th percentiles
+        "stages_us_p10_p90": {name: [round(float(np.percentile(v, 10)) * 1e3, 2), round(float(np.percentile(v, 90)) * 1e3, 2)]
+                              for name, v in (("draft_head", draft_ms), ("verify", verify_ms), ("accept", accept_ms),
+                                              ("commit", commit_ms))},
         "cycle_algorithmic_GBps": round(cycle_bytes * value / 1e9, 1),
         "tokens_per_s": round(float(nemit.sum().item()) * value, 1),
         "setup_s": round(setup_s, 1),
@@ -449,6 +453,18 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first /proc/cpuinfo entry), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(wl, head, hv, hd, n_cycles, with_commit, state_bytes):
     from oracle import mtp_oracle as O
     try:
@@ -482,7 +498,7 @@ def cpu_baseline(wl, head, hv, hd, n_cycles, with_commit, state_bytes):
     return {"value": round(done / el, 4), "unit": "cycles/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} whole cycles of the {wl.name} workload (numpy fp64, weights pre-converted "
                       f"to fp64 outside the timing), {el:.1f} s",
-            "blas": blas, "cpu": platform.processor() or platform.machine(),
+            "blas": blas, "cpu": cpu_model(),
             "host_cores_visible": len(os.sched_getaffinity(0))}
 
 
