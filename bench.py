@@ -58,6 +58,7 @@ def parse():
     ap.add_argument("--extra-cycles", type=int, default=30, help="cycles timed by each extra measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-commit", action="store_true", help="leave the commit out of the step")
+    ap.add_argument("--no-copy-peak", action="store_true", help="skip the 1 GiB copy-peak measurement")
     ap.add_argument("--row-major", action="store_true",
                     help="keep the head row-major instead of repacking it once into the tiled layout")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -446,6 +447,34 @@ def main():
             "cycles_per_s": round(args.extra_cycles / el, 2), "tokens_per_s": round(tot / el, 1),
             "mean_tokens_per_request_cycle": round(tot / (args.extra_cycles * B), 3),
             "planted_mean_depth": round(depth_sum / (n_sets * B), 3), "stages_us": pst}
+
+    # ---- measured copy peak: the library's own copy (the commit kernel) of a 512 MiB state,
+    #      best of 5, (read + write bytes) / time; the LM-head kernels' rates as a fraction of
+    #      it (torch's copy kernel reaches less: it is no ceiling for these kernels) ---------
+    if not args.no_copy_peak:
+        half = COPY_BYTES // 2
+        csnap = torch.empty(1, 2, half, dtype=torch.uint8, device=dev)
+        csnap.fill_(1)
+        clive = torch.empty(1, half, dtype=torch.uint8, device=dev)
+        cacc = torch.zeros(1, dtype=torch.int32, device=dev)
+        clen = torch.zeros(1, dtype=torch.int32, device=dev)
+        mtp.mtp_commit_state(1, 1, cacc, csnap, clive, half, None, 0, 0, 0, clen, stream)
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            mtp.mtp_commit_state(1, 1, cacc, csnap, clive, half, None, 0, 0, 0, clen, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3
+            best = t if best is None else min(best, t)
+        peak = 2 * half / best / 1e9
+        del csnap, clive
+        result["copy_peak"] = {"GBps": round(peak, 1),
+                               "kind": "mtp_commit_state copy of a 512 MiB state, (read + write) / time, best of 5"}
+        for key in ("roofline", "roofline_verify"):
+            result[key]["frac_of_copy_peak"] = round(result[key]["achieved"] / peak, 4)
 
     # ---- CPU baseline: the oracle, as it stands, on a bounded sample --------------
     if not args.no_cpu_baseline:
