@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="model_greedy", choices=["model_greedy", "q4_greedy", "q4_sampled", "exact_sampled", "batched_commit"])
+    ap.add_argument("--workload", default="model_greedy", choices=["model_greedy", "q4_greedy", "q4_sampled", "exact_sampled", "batched_commit",
+                                                      "tiny_greedy", "tiny_sampled"])
     ap.add_argument("--cpu-cycles", type=int, default=0, help="oracle cycles for the CPU baseline (0 = auto)")
     ap.add_argument("--event-every", type=int, default=10,
                     help="record per-kernel HIP events in every N-th timed cycle (each event is a queue packet "
@@ -210,21 +211,31 @@ def main():
     h_v, h_d = synth.make_hidden(rng, wl.B, wl.k, wl.d)
     hv = synth.encode_hidden(h_v, wl.htype)
     hd = synth.encode_hidden(h_d, wl.htype)
-    if wl.wtype == "bf16":
+    # the tiny workloads: fp32 head and hidden rows, row-major, no recurrent state (a cycle is
+    # k draft calls + verify + accept)
+    tiny = wl.wtype == "f32"
+
+    def dev_rows(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a if wl.htype == "f32" else a.view(np.int16)).to(dev)
+
+    if wl.wtype == "f32":
+        dh = mtp.Head(mtp.W_F32, wl.d, wl.V, torch.from_numpy(head.w).to(dev))
+    elif wl.wtype == "bf16":
         dh = mtp.Head(mtp.W_BF16, wl.d, wl.V, torch.from_numpy(head.w.view(np.int16)).to(dev))
     else:
         dh = mtp.Head(mtp.W_Q4A32, wl.d, wl.V, torch.from_numpy(head.w).to(dev),
                       torch.from_numpy(head.scale.view(np.int16)).to(dev),
                       torch.from_numpy(head.minv.view(np.int16)).to(dev))
-    if not args.row_major:
+    if not args.row_major and not tiny:
         # one-time weight preparation at load: fragment-major tiles (same numbers, same logits)
         dh = mtp.tiled_head(dh)
         torch.cuda.synchronize()
     B, k, nd, V, d, T = wl.B, wl.k, wl.n_draft, wl.V, wl.d, wl.temperature
     exact = T > 0 and wl.accept_rule == "exact"
     rule = mtp.ACCEPT_EXACT if exact else mtp.ACCEPT_RATIO
-    hv_t = torch.from_numpy(hv.view(np.int16)).to(dev)                          # [B][k+1][d]
-    hd_slots = [torch.from_numpy(np.ascontiguousarray(hd[:, i]).view(np.int16)).to(dev) for i in range(k)]
+    hv_t = dev_rows(hv)                                                          # [B][k+1][d]
+    hd_slots = [dev_rows(hd[:, i]) for i in range(k)]
     dtok = torch.zeros(B, k, dtype=torch.int32, device=dev)
     dst = mtp.row_stats_empty(B, k)
     # exact-match acceptance reads neither the draft logits nor the verify logits
@@ -238,7 +249,7 @@ def main():
     ws = mtp.workspace(max(mtp.workspace_bytes(mtp.OP_DRAFT, B, nd, B),
                            mtp.workspace_bytes(mtp.OP_VERIFY, B * (k + 1), V, B),
                            mtp.workspace_bytes(mtp.OP_ACCEPT, 0, V, B)))
-    with_commit = not args.no_commit
+    with_commit = not args.no_commit and not tiny
     state_bytes = STATE_LAYERS * STATE_HEADS * STATE_DIM * STATE_DIM * 4
     kv_row_bytes = KV_HEADS * KV_DIM * 2
     if with_commit:
@@ -313,8 +324,8 @@ def main():
     value = args.steps / elapsed
 
     # algorithmic bytes per launch (weights read once, hidden rows, outputs)
-    wrow = {"bf16": d * 2, "q4a32": d // 2 + 2 * 2 * (d // 32)}[wl.wtype]
-    hbytes = d * 2
+    wrow = {"f32": d * 4, "bf16": d * 2, "q4a32": d // 2 + 2 * 2 * (d // 32)}[wl.wtype]
+    hbytes = d * (4 if wl.htype == "f32" else 2)
     draft_bytes = nd * wrow + B * hbytes + B * (32 + 4) + (B * nd * 4 if dlg is not None else 0)
     verify_bytes = V * wrow + B * (k + 1) * hbytes + B * (k + 1) * 32 + (B * (k + 1) * V * 4 if vlg is not None else 0)
     commit_bytes = (2 * B * state_bytes) if with_commit else 0
@@ -355,11 +366,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.wtype == "bf16" else "q4a32",
+        "dtype": {"f32": "f32", "bf16": "bf16", "q4a32": "q4a32"}[wl.wtype],
         "data": "synthetic",
         "config": {"workload": args.workload, "d": d, "V": V, "n_draft": nd, "k": k, "batch": B,
                    "temperature": T, "accept_rule": wl.accept_rule if T > 0 else "exact (greedy)",
-                   "weights": wl.wtype, "layout": "row-major" if args.row_major else "tiled",
+                   "weights": wl.wtype, "layout": "row-major" if (args.row_major or tiny) else "tiled",
                    "accumulate": "fp32",
                    "step": f"{k} draft-head calls + verify ({B * (k + 1)} rows) + accept"
                            + (" + commit (36 MiB snapshot select, 12-layer KV trim)" if with_commit else "")},
@@ -379,6 +390,11 @@ def main():
         "tokens_per_s": round(float(nemit.sum().item()) * value, 1),
         "setup_s": round(setup_s, 1),
     }
+
+    if tiny:
+        for key in ("roofline", "roofline_verify"):
+            result[key]["note"] = ("the head (4 MiB, draft rows 1 MiB) stays in the caches: the tiny cycle is "
+                                   "latency-bound, its fraction of HBM bandwidth is not a target")
 
     # ---- draft head against HBM proper: rotate over copies of the head, so that no
     #      call finds the previous call's rows in the 256 MB last-level cache ------------
@@ -419,8 +435,7 @@ def main():
             alt = (tg + 1 + prng.integers(0, nd - 1, size=(B, k + 1))) % nd
             synth.plant_rows(head, pv, pd, depths, tg, alt)
             ev_, ed_ = synth.encode_hidden(pv, wl.htype), synth.encode_hidden(pd, wl.htype)
-            sets.append((torch.from_numpy(ev_.view(np.int16)).to(dev),
-                         [torch.from_numpy(np.ascontiguousarray(ed_[:, i]).view(np.int16)).to(dev) for i in range(k)]))
+            sets.append((dev_rows(ev_), [dev_rows(ed_[:, i]) for i in range(k)]))
             depth_sum += int(depths.sum())
         emitted = torch.zeros(B, dtype=torch.int64, device=dev)
         for c in range(n_sets):   # warm-up, also of the counter update (its first call loads a kernel)
