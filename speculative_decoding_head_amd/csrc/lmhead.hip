@@ -488,7 +488,7 @@ void mtp_verify_logits_kernel(LmheadLaunch p) {
 
 int lmhead_grid(int n_rows) {
   const int tiles = (n_rows + 15) / 16;
-  const int g = (tiles + 15) / 16;   // the workspace's partials per row: one per 16 tiles, at most 256
+  const int g = (tiles + 7) / 8;   // the workspace's partials per row: one per 8 tiles, at most 256
   return g < 1 ? 1 : (g > kMaxGrid ? kMaxGrid : g);
 }
 
