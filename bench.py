@@ -57,6 +57,10 @@ def parse():
                     help="after the timed region, time whole cycles whose acceptance depth is planted per "
                          "request with P(depth >= j) = alpha^j; 0 = skip")
     ap.add_argument("--extra-cycles", type=int, default=30, help="cycles timed by each extra measurement")
+    ap.add_argument("--adaptive-cycles", type=int, default=200,
+                    help="after the planted-acceptance cycles (one request only), run this many cycles whose "
+                         "width the native controller picks, and as many at the full width, both synchronising "
+                         "every cycle; 0 = skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-commit", action="store_true", help="leave the commit out of the step")
     ap.add_argument("--no-copy-peak", action="store_true", help="skip the 1 GiB copy-peak measurement")
@@ -257,7 +261,7 @@ def main():
         snaps = torch.randint(0, 256, (B, k + 1, state_bytes), dtype=torch.uint8, device=dev, generator=g)
         live = torch.zeros(B, state_bytes, dtype=torch.uint8, device=dev)
         # room for every cycle's accepted rows, so the trim never saturates at the cache end
-        kv_rows = KV_ROWS + (k + 1) * (args.warmup + args.steps + 16 + args.extra_cycles)
+        kv_rows = KV_ROWS + (k + 1) * (args.warmup + args.steps + 16 + args.extra_cycles + 2 * args.adaptive_cycles)
         kv = torch.zeros(B, KV_LAYERS, 2, kv_rows, kv_row_bytes, dtype=torch.uint8, device=dev)
         kv_len = torch.zeros(B, dtype=torch.int32, device=dev)
     # the position verify row 0 predicts: the committed length (exact-match rule)
@@ -462,6 +466,56 @@ def main():
             "cycles_per_s": round(args.extra_cycles / el, 2), "tokens_per_s": round(tot / el, 1),
             "mean_tokens_per_request_cycle": round(tot / (args.extra_cycles * B), 3),
             "planted_mean_depth": round(depth_sum / (n_sets * B), 3), "stages_us": pst}
+
+        # ---- adaptive verify width: the native controller picks k for every cycle from its
+        #      per-depth acceptance averages and its fitted cycle cost (the cycle's device time),
+        #      against the full width with the same per-cycle synchronisation (the controller
+        #      needs each cycle's outcome before it picks the next width) --------------------
+        if args.adaptive_cycles > 0 and B == 1:
+            def run_width(kk, c, hidden):
+                hv_c, hd_c = hidden
+                hv_k = hv_c[:, :kk + 1].contiguous()
+                smp = mtp.sampling(T, wl.eos, wl.philox_seed, c, 0, rule, positions if exact else None)
+                for i in range(kk):
+                    mtp.mtp_draft_head(dh, nd, hd_c[i], i, k, smp, dtok, dst, dlg, ws, stream)
+                # one request: the first kk + 1 verify rows of every buffer are a contiguous prefix
+                vst_k, out_k = vst[:, :kk + 1], out[:, :kk + 1]
+                vlg_k = None if vlg is None else vlg[:, :kk + 1]
+                mtp.mtp_verify_logits(dh, hv_k, kk, dtok, k, smp, vst_k, vlg_k, ws, stream)
+                mtp.mtp_accept_sample(B, kk, k, V, nd, smp, dtok, dst, dlg, vst_k, vlg_k, out_k, nacc, nemit, flg,
+                                      ws, stream)
+                if with_commit:
+                    mtp.mtp_commit_state(B, kk, nacc, snaps[:, :kk + 1], live, state_bytes, kv, KV_LAYERS, kv_rows,
+                                         kv_row_bytes, kv_len, stream)
+
+            aw = {"alpha": args.planted_alpha, "cycles": args.adaptive_cycles}
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for mode in ("adaptive", "full_width"):
+                ctl = mtp.WidthController(k_max=k)
+                hist, toks, dev_s = [0] * (k + 1), 0, 0.0
+                torch.cuda.synchronize()
+                t1 = time.perf_counter()
+                for c in range(args.adaptive_cycles):
+                    kk = ctl.choose() if mode == "adaptive" else k
+                    e0.record(stream)
+                    run_width(kk, c, sets[c % n_sets])
+                    e1.record(stream)
+                    e1.synchronize()
+                    sec = e0.elapsed_time(e1) * 1e-3
+                    ctl.observe(kk, nacc, flg, sec)
+                    toks += int(nemit.sum().item())
+                    hist[kk] += 1
+                    dev_s += sec
+                el = time.perf_counter() - t1
+                aw[mode] = {"tokens_per_s": round(toks / el, 1), "tokens_per_device_s": round(toks / dev_s, 1),
+                            "mean_tokens_per_cycle": round(toks / args.adaptive_cycles, 3),
+                            "width_histogram": {str(w): n for w, n in enumerate(hist) if n}}
+                if mode == "adaptive":
+                    aw[mode].update({"final_width": ctl.choose(),
+                                     "acceptance_by_depth": [round(a, 3) for a in ctl.alpha[:k]],
+                                     "cost_fit_us": {"c0": round(ctl.cost(0) * 1e6, 1),
+                                                     "c1": round((ctl.cost(1) - ctl.cost(0)) * 1e6, 1)}})
+            result["adaptive_width"] = aw
 
     # ---- measured copy peak: the library's own copy (the commit kernel) of a 512 MiB state,
     #      best of 5, (read + write bytes) / time; the LM-head kernels' rates as a fraction of
