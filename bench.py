@@ -61,6 +61,10 @@ def parse():
                     help="after the planted-acceptance cycles (one request only), run this many cycles whose "
                          "width the native controller picks, and as many at the full width, both synchronising "
                          "every cycle; 0 = skip")
+    ap.add_argument("--draft-ids", type=int, default=0, metavar="N_TOP",
+                    help="draft from an id list instead of the first n_draft ids: the N_TOP highest ids (a "
+                         "special-token block at the end of the vocabulary) plus the lowest ones, n_draft in all, "
+                         "gathered once into their own head; 0 = the first n_draft ids")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-commit", action="store_true", help="leave the commit out of the step")
     ap.add_argument("--no-copy-peak", action="store_true", help="skip the 1 GiB copy-peak measurement")
@@ -231,11 +235,23 @@ def main():
         dh = mtp.Head(mtp.W_Q4A32, wl.d, wl.V, torch.from_numpy(head.w).to(dev),
                       torch.from_numpy(head.scale.view(np.int16)).to(dev),
                       torch.from_numpy(head.minv.view(np.int16)).to(dev))
+    B, k, nd, V, d, T = wl.B, wl.k, wl.n_draft, wl.V, wl.d, wl.temperature
+    # draft vocabulary: the first nd ids, or an ascending id list gathered once into its own
+    # head (the draft head reports vocabulary ids; acceptance looks q up through row_of)
+    draft_ids = row_of = None
+    ddh = dh
+    if args.draft_ids > 0:
+        n_top = min(args.draft_ids, nd)
+        draft_ids = np.concatenate([np.arange(0, nd - n_top), np.arange(V - n_top, V)]).astype(np.int32)
+        ddh = mtp.gather_rows(dh, torch.from_numpy(draft_ids).to(dev))
+        ro = np.full(V, -1, np.int32)
+        ro[draft_ids] = np.arange(nd, dtype=np.int32)
+        row_of = torch.from_numpy(ro).to(dev)
     if not args.row_major and not tiny:
         # one-time weight preparation at load: fragment-major tiles (same numbers, same logits)
         dh = mtp.tiled_head(dh)
+        ddh = dh if draft_ids is None else mtp.tiled_head(ddh)
         torch.cuda.synchronize()
-    B, k, nd, V, d, T = wl.B, wl.k, wl.n_draft, wl.V, wl.d, wl.temperature
     exact = T > 0 and wl.accept_rule == "exact"
     rule = mtp.ACCEPT_EXACT if exact else mtp.ACCEPT_RATIO
     hv_t = dev_rows(hv)                                                          # [B][k+1][d]
@@ -278,13 +294,14 @@ def main():
         if events is not None:
             events[0].record(stream)
         for i in range(k):
-            mtp.mtp_draft_head(dh, nd, hd_c[i], i, k, smp, dtok, dst, dlg, ws, stream)
+            mtp.mtp_draft_head(ddh, nd, hd_c[i], i, k, smp, dtok, dst, dlg, ws, stream)
         if events is not None:
             events[1].record(stream)
         mtp.mtp_verify_logits(dh, hv_c, k, dtok, k, smp, vst, vlg, ws, stream)
         if events is not None:
             events[2].record(stream)
-        mtp.mtp_accept_sample(B, k, k, V, nd, smp, dtok, dst, dlg, vst, vlg, out, nacc, nemit, flg, ws, stream)
+        mtp.mtp_accept_sample(B, k, k, V, nd, smp, dtok, dst, dlg, vst, vlg, out, nacc, nemit, flg, ws, stream,
+                              draft_row_of=row_of)
         if events is not None:
             events[3].record(stream)
         if with_commit:
@@ -376,6 +393,9 @@ def main():
                    "temperature": T, "accept_rule": wl.accept_rule if T > 0 else "exact (greedy)",
                    "weights": wl.wtype, "layout": "row-major" if (args.row_major or tiny) else "tiled",
                    "accumulate": "fp32",
+                   "draft_vocabulary": (f"id list: the lowest {nd - min(args.draft_ids, nd):,} and the highest "
+                                        f"{min(args.draft_ids, nd):,} ids" if draft_ids is not None else
+                                        f"the first {nd:,} ids"),
                    "step": f"{k} draft-head calls + verify ({B * (k + 1)} rows) + accept"
                            + (" + commit (36 MiB snapshot select, 12-layer KV trim)" if with_commit else "")},
         "roofline": roofline,
@@ -403,10 +423,10 @@ def main():
     # ---- draft head against HBM proper: rotate over copies of the head, so that no
     #      call finds the previous call's rows in the 256 MB last-level cache ------------
     if args.rotate_heads > 1:
-        copies = [dh] + [mtp.Head(dh.wtype, dh.d, dh.vocab, dh.w.clone(),
-                                  None if dh.scale is None else dh.scale.clone(),
-                                  None if dh.minv is None else dh.minv.clone())
-                         for _ in range(args.rotate_heads - 1)]
+        copies = [ddh] + [mtp.Head(ddh.wtype, ddh.d, ddh.vocab, ddh.w.clone(),
+                                   None if ddh.scale is None else ddh.scale.clone(),
+                                   None if ddh.minv is None else ddh.minv.clone(), ddh.row_ids)
+                          for _ in range(args.rotate_heads - 1)]
         smp = mtp.sampling(T, wl.eos, wl.philox_seed, 0, 0, rule, positions if exact else None)
         n = args.extra_cycles * k
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -437,6 +457,8 @@ def main():
             depths = np.minimum(prng.geometric(1.0 - args.planted_alpha, size=B) - 1, k)
             tg = prng.integers(0, nd, size=(B, k + 1))
             alt = (tg + 1 + prng.integers(0, nd - 1, size=(B, k + 1))) % nd
+            if draft_ids is not None:   # planted tokens the draft vocabulary holds
+                tg, alt = draft_ids[tg], draft_ids[alt]
             synth.plant_rows(head, pv, pd, depths, tg, alt)
             ev_, ed_ = synth.encode_hidden(pv, wl.htype), synth.encode_hidden(pd, wl.htype)
             sets.append((dev_rows(ev_), [dev_rows(ed_[:, i]) for i in range(k)]))
@@ -477,13 +499,13 @@ def main():
                 hv_k = hv_c[:, :kk + 1].contiguous()
                 smp = mtp.sampling(T, wl.eos, wl.philox_seed, c, 0, rule, positions if exact else None)
                 for i in range(kk):
-                    mtp.mtp_draft_head(dh, nd, hd_c[i], i, k, smp, dtok, dst, dlg, ws, stream)
+                    mtp.mtp_draft_head(ddh, nd, hd_c[i], i, k, smp, dtok, dst, dlg, ws, stream)
                 # one request: the first kk + 1 verify rows of every buffer are a contiguous prefix
                 vst_k, out_k = vst[:, :kk + 1], out[:, :kk + 1]
                 vlg_k = None if vlg is None else vlg[:, :kk + 1]
                 mtp.mtp_verify_logits(dh, hv_k, kk, dtok, k, smp, vst_k, vlg_k, ws, stream)
                 mtp.mtp_accept_sample(B, kk, k, V, nd, smp, dtok, dst, dlg, vst_k, vlg_k, out_k, nacc, nemit, flg,
-                                      ws, stream)
+                                      ws, stream, draft_row_of=row_of)
                 if with_commit:
                     mtp.mtp_commit_state(B, kk, nacc, snaps[:, :kk + 1], live, state_bytes, kv, KV_LAYERS, kv_rows,
                                          kv_row_bytes, kv_len, stream)
