@@ -57,6 +57,9 @@ def parse():
                     help="after the timed region, time whole cycles whose acceptance depth is planted per "
                          "request with P(depth >= j) = alpha^j; 0 = skip")
     ap.add_argument("--extra-cycles", type=int, default=30, help="cycles timed by each extra measurement")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="after the timed region, time the same K cycles this many more times and report the "
+                         "spread of their rates (value stays the first window)")
     ap.add_argument("--adaptive-cycles", type=int, default=200,
                     help="after the planted-acceptance cycles (one request only), run this many cycles whose "
                          "width the native controller picks, and as many at the full width, both synchronising "
@@ -277,7 +280,8 @@ def main():
         snaps = torch.randint(0, 256, (B, k + 1, state_bytes), dtype=torch.uint8, device=dev, generator=g)
         live = torch.zeros(B, state_bytes, dtype=torch.uint8, device=dev)
         # room for every cycle's accepted rows, so the trim never saturates at the cache end
-        kv_rows = KV_ROWS + (k + 1) * (args.warmup + args.steps + 16 + args.extra_cycles + 2 * args.adaptive_cycles)
+        kv_rows = KV_ROWS + (k + 1) * (args.warmup + args.steps * (1 + args.repeats) + 16 + args.extra_cycles
+                                       + 2 * args.adaptive_cycles)
         kv = torch.zeros(B, KV_LAYERS, 2, kv_rows, kv_row_bytes, dtype=torch.uint8, device=dev)
         kv_len = torch.zeros(B, dtype=torch.int32, device=dev)
     # the position verify row 0 predicts: the committed length (exact-match rule)
@@ -342,6 +346,15 @@ def main():
     accept_ms = [evs[s][2].elapsed_time(evs[s][3]) for s in timed]
     commit_ms = ([evs[s][3].elapsed_time(evs[s][4]) for s in timed] if with_commit else [0.0])
     ms_per_step = elapsed * 1e3 / args.steps
+    # stability: the same K cycles timed again in further windows (not part of `value`)
+    repeat_rates = []
+    for r in range(args.repeats):
+        torch.cuda.synchronize()
+        t_r = time.perf_counter()
+        for s_ in range(args.steps):
+            cycle(args.warmup + args.steps * (r + 1) + s_)
+        torch.cuda.synchronize()
+        repeat_rates.append(args.steps / (time.perf_counter() - t_r))
     value = args.steps / elapsed
 
     # algorithmic bytes per launch (weights read once, hidden rows, outputs)
@@ -411,6 +424,9 @@ def main():
                               for name, v in (("draft_head", draft_ms), ("verify", verify_ms), ("accept", accept_ms),
                                               ("commit", commit_ms))},
         "cycle_algorithmic_GBps": round(cycle_bytes * value / 1e9, 1),
+        "repeat_cycles_per_s": ({"windows": len(repeat_rates), "min": round(min(repeat_rates), 2),
+                                 "median": round(float(np.median(repeat_rates)), 2), "max": round(max(repeat_rates), 2)}
+                                if repeat_rates else None),
         "tokens_per_s": round(float(nemit.sum().item()) * value, 1),
         "setup_s": round(setup_s, 1),
     }
