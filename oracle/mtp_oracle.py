@@ -52,7 +52,20 @@ Readings where the pages are silent (each is a stated choice, listed with the de
 
 Where floating point decides an integer (an argmax, the ratio test), the decision is
 taken in fp32, the kernel's precision, on the fp64 quantities rounded once to fp32.
-Margins for the near-tie flags are measured in fp64.
+
+Near ties.  A GPU logit may differ from the oracle's by up to the logit tolerance delta
+(the comparison's hard check on every materialised logit).  A decision is flagged -- the
+GPU may take it either way -- when its margin, measured in fp64 in the units of its own
+score, is within what that tolerance moves the score:
+  * an argmax of logits z: top-1 minus top-2 <= delta;
+  * an argmax of z/T + Gumbel (draft sample, bonus, the trunk's own sample): top-1 minus
+    top-2 <= delta/T;
+  * the ratio test: |ln u + ln q(t) - ln p(t)| <= delta/T;
+  * the residual pick argmax(ln max(0, p - q) + Gumbel): every ln p(x) and ln q(x) may
+    move by eps = 2 delta/T (delta/T from the logit, delta/T from the row's log-sum-exp);
+    under such moves max(0, p - q) ranges over an interval per id, and the pick is
+    flagged when the least score of the picked id does not exceed the greatest score of
+    some other id.  An empty residual is flagged when such moves can give it mass.
 """
 from __future__ import annotations
 
@@ -251,12 +264,82 @@ def top2_gap(scores: np.ndarray) -> np.ndarray:
     return np.where(np.isfinite(part[..., 1]), gap, np.inf)
 
 
+def argmax_margin(zs: np.ndarray, rflags: np.ndarray) -> np.ndarray:
+    """Top-2 gap of sanitised logits for the argmax; infinite for a row that held +inf,
+    whose argmax is its lowest +inf id by an exact rule on exact values (the sanitised +inf
+    ids are all exactly 0), which no logit tolerance can turn."""
+    gap = top2_gap(zs)
+    return np.where((np.asarray(rflags) & ROW_POSINF) != 0, np.inf, gap)
+
+
 def _f32_add(a, b):
     return np.asarray(a, dtype=np.float64).astype(F32) + np.asarray(b, dtype=np.float64).astype(F32)
 
 
 def _teff(T: float) -> float:
     return T if T > 0 else 1.0
+
+
+# ----------------------------------------------------------------------------------
+# near-tie flags (decisions the logit tolerance delta can turn either way)
+# ----------------------------------------------------------------------------------
+def score_tolerance(delta: float, T: float) -> float:
+    """What a logit tolerance delta moves a score z/T + Gumbel by: delta/T (delta at T = 0,
+    where the score is the logit itself)."""
+    return delta / T if T > 0 else delta
+
+
+def gap_near_tie(gap, tol: float) -> np.ndarray:
+    """An argmax whose top-1 minus top-2 score is within the score's tolerance."""
+    return np.asarray(gap, dtype=np.float64) <= tol
+
+
+def ratio_near_tie(margin, delta: float, T: float) -> np.ndarray:
+    """The ratio test u*q(t) <= p(t) with |ln u + ln q(t) - ln p(t)| <= delta/T."""
+    m = np.asarray(margin, dtype=np.float64)
+    with np.errstate(invalid="ignore"):
+        return np.isfinite(m) & (np.abs(m) <= delta / T)
+
+
+def residual_logprob_shift(delta: float, T: float) -> float:
+    """How far a logit tolerance delta can move ln p(x) = z_x/T - lse(z/T): delta/T through
+    z_x and delta/T through the log-sum-exp (which moves by at most the largest logit
+    move)."""
+    return 2.0 * delta / T
+
+
+def residual_bounds(lp, lq, eps: float):
+    """Least and greatest ln max(0, p' - q') over ln p' in [lp - eps, lp + eps] and
+    ln q' in [lq - eps, lq + eps] (-inf where the residual can vanish / is always 0)."""
+    lp = np.asarray(lp, dtype=np.float64)
+    lq = np.asarray(lq, dtype=np.float64)
+    lo_p, hi_q = lp - eps, lq + eps          # smallest p' - q'
+    hi_p, lo_q = lp + eps, lq - eps          # largest p' - q'
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        lo = np.where(hi_q < lo_p, lo_p + np.log1p(-np.exp(hi_q - lo_p)), NEG_INF)
+        hi = np.where(lo_q < hi_p, hi_p + np.log1p(-np.exp(lo_q - hi_p)), NEG_INF)
+    return lo, hi
+
+
+def residual_near_tie(lp, lq, G, pick, delta: float, T: float) -> np.ndarray:
+    """Residual picks [n] (argmax of ln max(0, p - q) + G over rows [n][V]) that moves of
+    ln p and ln q within residual_logprob_shift could change: the picked id's least score
+    is not above the greatest score of some other id."""
+    lo, hi = residual_bounds(lp, lq, residual_logprob_shift(delta, T))
+    G = np.asarray(G, dtype=np.float64)
+    rows = np.arange(G.shape[0])
+    pick = np.asarray(pick, dtype=np.int64)
+    s_lo = lo[rows, pick] + G[rows, pick]
+    s_hi = hi + G
+    s_hi[rows, pick] = NEG_INF
+    return s_lo <= s_hi.max(axis=-1)
+
+
+def empty_residual_near_tie(lp, lq, delta: float, T: float) -> np.ndarray:
+    """Rows [n][V] with an empty residual (p <= q everywhere) that moves within
+    residual_logprob_shift could give mass."""
+    _, hi = residual_bounds(lp, lq, residual_logprob_shift(delta, T))
+    return (hi > NEG_INF).any(axis=-1)
 
 
 # ----------------------------------------------------------------------------------
@@ -281,14 +364,14 @@ def draft_rows(W64: np.ndarray, n_draft: int, h: np.ndarray, T: float, seed: int
     if T > 0:
         G = gumbel_noise(seed, STREAM_DRAFT, slot, b_ids, cycle, rows.size, ids=rows)
         local = argmax_lowest_f32(_f32_add(zs / T, G))
-        margin, thr = top2_gap(zs / T + G), delta / T
+        margin = top2_gap(zs / T + G)
     else:
         local = argmax_lowest_f32(zs)
-        margin, thr = top2_gap(zs), delta
+        margin = argmax_margin(zs, rflags)
     token = np.where(local >= 0, rows[np.maximum(local, 0)], -1)
     z_tok = np.where(local >= 0, np.take_along_axis(zs, np.maximum(local, 0)[:, None], 1)[:, 0], NEG_INF)
     return dict(token=token, max=zs.max(axis=-1), lse=logsumexp_rows(zs / _teff(T)), z_tok=z_tok,
-                flags=rflags, logits=z, margin=margin, near_tie=margin <= thr)
+                flags=rflags, logits=z, margin=margin, near_tie=gap_near_tie(margin, score_tolerance(delta, T)))
 
 
 # ----------------------------------------------------------------------------------
@@ -310,7 +393,7 @@ def verify_rows(W64: np.ndarray, h_v: np.ndarray, drafts, T: float, seed: int, c
     V = z.shape[-1]
     zs, rflags = sanitize(z)
     y = argmax_lowest_f32(zs)
-    y_margin = top2_gap(zs)
+    y_margin = argmax_margin(zs, rflags)
     if T > 0 and positions is not None:
         sample = np.empty((B, K1), dtype=np.int64)
         s_margin = np.empty((B, K1))
@@ -333,7 +416,9 @@ def verify_rows(W64: np.ndarray, h_v: np.ndarray, drafts, T: float, seed: int, c
             ok = (t >= 0) & (t < V)
             z_tok[:, i] = np.where(ok, zs[np.arange(B), i, np.clip(t, 0, V - 1)], NEG_INF)
     return dict(argmax=y, sample=sample, max=zs.max(axis=-1), lse=logsumexp_rows(zs / _teff(T)),
-                z_tok=z_tok, flags=rflags, logits=z, y_margin=y_margin, s_margin=s_margin)
+                z_tok=z_tok, flags=rflags, logits=z, y_margin=y_margin, s_margin=s_margin,
+                y_near_tie=gap_near_tie(y_margin, delta),
+                s_near_tie=gap_near_tie(s_margin, score_tolerance(delta, T)))
 
 
 # ----------------------------------------------------------------------------------
@@ -393,7 +478,7 @@ def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int
     Te = _teff(T)
     lse_v = logsumexp_rows(zv / Te)
     y = argmax_lowest_f32(zv)
-    y_margin = top2_gap(zv)
+    y_margin = argmax_margin(zv, vflags)
     exact = T > 0 and rule == RULE_EXACT
     if exact:
         ys, ys_margin = np.asarray(target["sample"]), np.asarray(target["s_margin"])
@@ -438,7 +523,7 @@ def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int
         tc = np.clip(t, 0, V - 1)
         if exact:
             ok = t_ok & (t == ys[:, i])
-            mark_tie(active & (ys_margin[:, i] <= delta / T), i)
+            mark_tie(active & gap_near_tie(ys_margin[:, i], score_tolerance(delta, T)), i)
         elif T > 0:
             with np.errstate(invalid="ignore"):   # a non-finite target row gives NaN here, flagged above
                 lp_t = np.where(t_ok, zv[rows, i, tc] / T - lse_v[:, i], NEG_INF)
@@ -449,11 +534,11 @@ def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int
             u = uniform_accept(philox_words(seed, STREAM_ACCEPT, i, b_ids, cycle, 0))
             ok = t_ok & accept_test(lp_t, lq_t, u)
             with np.errstate(invalid="ignore"):
-                m = np.abs(np.log(u) + lq_t - lp_t)
-            mark_tie(active & t_ok & np.isfinite(m) & (m <= delta / T), i)
+                m = np.log(u) + lq_t - lp_t
+            mark_tie(active & t_ok & ratio_near_tie(m, delta, T), i)
         else:
             ok = t_ok & (t == y[:, i])
-            mark_tie(active & (y_margin[:, i] <= delta), i)
+            mark_tie(active & gap_near_tie(y_margin[:, i], delta), i)
         rej = active & ~ok
         n_accept[rej] = i
         stop_kind[rej] = 0
@@ -497,17 +582,9 @@ def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int
         pick_p, gap_p = gumbel_pick(zv[sel, a] / T, G)
         last[sel] = np.where(has_mass, pick_r, pick_p)
         flags[sel[~has_mass]] |= ACC_RESID_FALLBACK
-        # near-tie of the residual pick: gap <= e(top1) + e(top2), e = (delta/T)(p+q)/r
-        score = ln_r + G
-        top = np.argsort(-score, axis=-1, kind="stable")[:, :2]
-        s1 = np.take_along_axis(score, top, axis=-1)
-        with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
-            p = np.exp(np.take_along_axis(lp, top, -1))
-            q = np.exp(np.take_along_axis(lq, top, -1))
-            r = np.exp(np.take_along_axis(ln_r, top, -1))
-            e = (delta / T) * (p + q) / np.where(r > 0, r, np.inf)
-        tie_r = np.isfinite(s1[:, 1]) & (s1[:, 0] - s1[:, 1] <= e[:, 0] + e[:, 1])
-        tie = np.where(has_mass, tie_r, gap_p <= delta / T)
+        tie_r = residual_near_tie(lp, lq, G, np.maximum(pick_r, 0), delta, T)
+        tie_p = empty_residual_near_tie(lp, lq, delta, T) | gap_near_tie(gap_p, score_tolerance(delta, T))
+        tie = np.where(has_mass, tie_r, tie_p)
         mark_tie(np.isin(rows, sel[tie]), a)
 
     sel = np.nonzero(stop_kind == 2)[0]
@@ -515,14 +592,14 @@ def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int
     if sel.size:
         if exact:
             last[sel] = ys[sel, k]
-            mark_tie(np.isin(rows, sel[ys_margin[sel, k] <= delta / T]), k)
+            mark_tie(np.isin(rows, sel[gap_near_tie(ys_margin[sel, k], score_tolerance(delta, T))]), k)
         elif T > 0:
             G = gumbel_noise(seed, STREAM_RESAMPLE, k, b_ids[sel], cycle, V)
             last[sel], gap = gumbel_pick(zv[sel, k] / T, G)
-            mark_tie(np.isin(rows, sel[gap <= delta / T]), k)
+            mark_tie(np.isin(rows, sel[gap_near_tie(gap, score_tolerance(delta, T))]), k)
         else:
             last[sel] = y[sel, k]
-            mark_tie(np.isin(rows, sel[y_margin[sel, k] <= delta]), k)
+            mark_tie(np.isin(rows, sel[gap_near_tie(y_margin[sel, k], delta)]), k)
     flags[stop_kind == 3] |= ACC_ROW_INVALID
 
     # emitted block: the accepted drafts, then the correction / bonus / EOS token
