@@ -11,7 +11,7 @@ import speculative_decoding_head_amd as mtp
 import synth
 from gpu_cycle import GpuCycle, dev_head, dev_hidden
 from oracle import mtp_oracle as O
-from parity import check_cycle
+from parity import add_results, check_cycle, check_excluded
 
 pytestmark = pytest.mark.gpu
 
@@ -107,6 +107,7 @@ def test_id_list_cycles_with_planted_depths(wtype, T, rule):
                   draft_row_of=_row_of(ids))
     positions = rng.integers(0, 1 << 16, size=B)
     orule = O.RULE_EXACT if rule == mtp.ACCEPT_EXACT else O.RULE_RATIO
+    total = None
     for cyc in range(6):
         h_v, h_d = synth.make_hidden(rng, B, k, D)
         depths = [(cyc + 2 * b) % (k + 1) for b in range(B)]
@@ -118,6 +119,8 @@ def test_id_list_cycles_with_planted_depths(wtype, T, rule):
                     rule=orule, positions=positions, draft_ids=ids)
         gc.set_positions(positions)
         g = gc.run(dev_hidden(hd), dev_hidden(hv), cycle=cyc)
-        check_cycle(g, o, T, delta, tag=f"{wtype} T{T} rule{rule} cycle {cyc}")
+        total = add_results(total, check_cycle(g, o, T, delta, tag=f"{wtype} T{T} rule{rule} cycle {cyc}",
+                                               rule=orule, bound=False))
         assert np.all(np.isin(g["drafts"][g["drafts"] >= 0], ids))
         positions = positions + g["n_emit"]
+    check_excluded(total, f"id list {wtype} T{T} rule{rule}")

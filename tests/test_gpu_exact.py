@@ -16,7 +16,7 @@ import speculative_decoding_head_amd as mtp
 import synth
 from gpu_cycle import GpuCycle, dev_head, dev_hidden
 from oracle import mtp_oracle as O
-from parity import check_cycle, check_verify
+from parity import add_results, check_cycle, check_excluded, check_verify
 
 pytestmark = pytest.mark.gpu
 
@@ -98,7 +98,7 @@ def test_exact_rule_cycles_with_planted_depths(wtype, B):
     delta = 1e-4 if wtype == "f32" else 2e-2
     gc = GpuCycle(dev_head(head), ND, B, k, T, seed=seed, eos=eos, rule=mtp.ACCEPT_EXACT)
     positions = rng.integers(0, 1 << 16, size=B)
-    seen, flagged = set(), 0
+    seen, total = set(), None
     for cyc in range(8):
         h_v, h_d = synth.make_hidden(rng, B, k, D)
         depths = [(cyc + 3 * b) % (k + 1) for b in range(B)]
@@ -112,8 +112,8 @@ def test_exact_rule_cycles_with_planted_depths(wtype, B):
                     rule=O.RULE_EXACT, positions=positions)
         gc.set_positions(positions)
         g = gc.run(dev_hidden(hd), dev_hidden(hv), cycle=cyc)
-        r = check_cycle(g, o, T, delta, tag=f"{wtype} B{B} cycle {cyc}")
-        flagged += r["excluded"]
+        total = add_results(total, check_cycle(g, o, T, delta, tag=f"{wtype} B{B} cycle {cyc}", rule="exact",
+                                               bound=False))
         seen.update(int(a) for a in g["n_accept"])
         # the emitted tokens are the trunk's draws: drafts up to the first mismatch, then the draw
         vs = g["vstats"]
@@ -124,4 +124,4 @@ def test_exact_rule_cycles_with_planted_depths(wtype, B):
                 assert g["tokens"][b, a] == vs["sample"][b, a]
         positions = positions + g["n_emit"]
     assert len(seen) >= 4
-    assert flagged <= 2
+    check_excluded(total, f"{wtype} B{B}")

@@ -16,7 +16,7 @@ import speculative_decoding_head_amd as mtp
 import synth
 from gpu_cycle import GpuCycle, dev_head, dev_hidden
 from oracle import mtp_oracle as O
-from parity import check_cycle, close
+from parity import add_results, check_cycle, check_excluded, close
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -66,12 +66,40 @@ def _run(wl, W, dh, hv, hd, T, seed, cycle, planted=None):
     return g, o
 
 
+def _raw_requests(wl, hv, hd, n=16):
+    """The bench's own request (raw hidden rows of the model-scale workload) and n - 1 more
+    raw requests of the same distribution: [n][k+1][d], [n][k][d] bf16 bits."""
+    rng = np.random.default_rng(wl.seed + 1000)
+    h_v, h_d = synth.make_hidden(rng, n - 1, wl.k, wl.d)
+    return (np.concatenate([hv, synth.encode_hidden(h_v, "bf16")]),
+            np.concatenate([hd, synth.encode_hidden(h_d, "bf16")]))
+
+
+def _raw_cycles(wl, W, dh, hv, hd, T, seed, cycle, tag):
+    """One cycle per request in the bench's launch configuration (one request per call,
+    request b drawing as request b), all requests through the oracle at once; the near-tie
+    budget is checked over all of them."""
+    HV, HD = _raw_requests(wl, hv, hd)
+    n = HV.shape[0]
+    o = O.cycle(W, wl.n_draft, O.hidden_f64(HD, "bf16"), O.hidden_f64(HV, "bf16"), T, seed, cycle, -1, DELTA)
+    gc = GpuCycle(dh, wl.n_draft, 1, wl.k, T, seed=seed)
+    gs = [gc.run(dev_hidden(HD[b:b + 1]), dev_hidden(HV[b:b + 1]), cycle=cycle, request_base=b) for b in range(n)]
+    g = {key: np.concatenate([x[key] for x in gs]) for key in ("drafts", "tokens", "n_accept", "n_emit", "flags")}
+    for key in ("dstats", "vstats"):
+        g[key] = {f: np.concatenate([x[key][f] for x in gs]) for f in gs[0][key]}
+    if T > 0:
+        g["logits"] = np.concatenate([x["logits"] for x in gs])
+        g["draft_logits"] = np.concatenate([x["draft_logits"] for x in gs])
+    r = check_cycle(g, o, T, DELTA, tag=tag)
+    return g, o, r
+
+
 def test_model_greedy_cycle(bf16_model):
-    # the bench's exact inputs: raw (unplanted) hidden rows of the model-scale workload
+    # the bench's exact inputs (request 0) and 15 more raw requests: independent hidden rows
+    # reject at row 0, the decisions are the first draft and the verify argmax of row 0
     wl, (hv, hd), head, W, dh = bf16_model
-    g, o = _run(wl, W, dh, hv, hd, 0.0, 0, 0)
-    r = check_cycle(g, o, 0.0, DELTA, tag="model greedy")
-    print("flagged near ties:", r)
+    g, o, r = _raw_cycles(wl, W, dh, hv, hd, 0.0, 0, 0, "model greedy raw")
+    assert r["requests"] == 16
 
 
 @pytest.mark.parametrize("depth", [0, 3, 7])
@@ -155,8 +183,7 @@ def test_commit_at_model_state_size():
 def test_model_tiled_head_cycle(bf16_tiled, T):
     # the bench's head layout: tiled bf16, raw workload rows and a sampled cycle
     wl, (hv, hd), head, W, dh = bf16_tiled
-    g, o = _run(wl, W, dh, hv, hd, T, 1234, 2)
-    check_cycle(g, o, T, DELTA, tag=f"model tiled T{T}")
+    g, o, _ = _raw_cycles(wl, W, dh, hv, hd, T, 1234, 2, f"model tiled T{T}")
     if T > 0:
         assert np.abs(g["logits"].astype(np.float64) - o["verify"]["logits"]).max() <= DELTA
 
