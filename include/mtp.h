@@ -44,11 +44,16 @@
 extern "C" {
 #endif
 
-#define MTP_ABI_VERSION 2
+#define MTP_ABI_VERSION 3
 
 /* ---------------------------------------------------------------------------------- */
 /* status codes                                                                        */
 /* ---------------------------------------------------------------------------------- */
+/* Invalid input is reported, never crashed on: the loader commit of llama.cpp PR
+ * "qwen4exp : port NextN/MTP speculative decoding to master" (the PR body) makes a bad
+ * drafter load stop with a clear message where it used to segfault.  Every call here
+ * checks its arguments first and returns one of these codes; it never aborts, throws or
+ * touches memory it was not given. */
 typedef enum mtp_status {
   MTP_OK = 0,
   MTP_ERR_NULL = -1,      /* a required pointer is NULL                                 */
@@ -177,13 +182,20 @@ typedef struct mtp_row_stats {
 #define MTP_ACC_NONFINITE_TARGET 0x10u /* a target row examined held NaN/+-inf           */
 #define MTP_ACC_NONFINITE_DRAFT 0x20u  /* a draft row examined held NaN/+-inf            */
 #define MTP_ACC_DRAFT_INVALID 0x40u    /* a draft token was -1 (all -inf draft row)      */
+#define MTP_ACC_EOS_DRAFT 0x80u        /* the block ended on an accepted EOS draft: draft
+                                          n_accept+1 was EOS and was accepted (with EOS
+                                          alone, the EOS may be a correction or bonus)   */
 
 /* ---------------------------------------------------------------------------------- */
 /* workspace                                                                           */
 /* ---------------------------------------------------------------------------------- */
 typedef enum mtp_op { MTP_OP_DRAFT = 0, MTP_OP_VERIFY = 1, MTP_OP_ACCEPT = 2 } mtp_op;
 
-/* Bytes of device workspace an op needs.  rows = hidden rows of the call (draft: B,
+/* Bytes of device workspace an op needs (DS4Server issue "Add Qwen3.8 Flash Next native
+ * MTP speculation", section "Implementation": draft history, verify width, allocator
+ * caches and temporary buffers are bounded and counted in memory admission; this is that
+ * bound for the temporaries, so a caller can admit a request before running it).
+ * rows = hidden rows of the call (draft: B,
  * verify: B*(k+1)); n_vocab_rows = rows of the head it scores (draft: n_draft, verify
  * and accept: vocab); B = requests.  The workspace holds per-block partial results and
  * completion counters.  It must be 256-byte aligned and zero-filled once after it is
@@ -287,9 +299,17 @@ int mtp_commit_state(int32_t B, int32_t k, const int32_t* n_accept, const void* 
  * only, no device work.  The metrics the PR reports (drafted and accepted tokens,
  * verifier passes, acceptance depths) are its counters.
  *   alpha[j]  exponential moving average (weight `decay` per observation) of "draft j+1
- *             was accepted", over cycles that reached draft j+1; a block that ended with
- *             EOS or at an unusable target row leaves its stopping depth untouched;
- *   E(k)      = 1 + sum_{i=1..k} prod_{j<i} alpha[j]   (expected tokens of a k-draft cycle);
+ *             was accepted", over cycles that decided draft j+1: accepted (an accepted EOS
+ *             draft, MTP_ACC_EOS_DRAFT, included) or rejected (an EOS correction
+ *             included); a block that ended at an unusable target row leaves its stopping
+ *             depth untouched;
+ *   weight[j] recency of depth j: each request-cycle multiplies every weight by
+ *             (1 - decay) and adds 1 at each depth it decided;
+ *   a[j]      = alpha[j] where weight[j] >= 1/2, else a[j-1] (a[0] = alpha[0]): a depth
+ *             not decided recently is estimated by the depth before it, an optimistic
+ *             estimate that makes the controller explore deeper drafts when acceptance
+ *             rises;
+ *   E(k)      = 1 + sum_{i=1..k} prod_{j<i} a[j]   (expected tokens of a k-draft cycle);
  *   c(k)      = c0 + c1 k, least squares over the observed (k, seconds) pairs with weights
  *             decaying by (1 - decay) per observation; fewer than two distinct widths:
  *             c1 = slope_prior * c0; a negative fitted slope is taken as 0; no timing
@@ -302,6 +322,7 @@ typedef struct mtp_width_ctl {
   double decay;                  /* (0, 1]                                                */
   double slope_prior;            /* >= 0: c1 / c0 until two widths have been timed         */
   double alpha[7];
+  double weight[7];              /* recency of each depth's estimate                        */
   double sw, sk, skk, st, skt;   /* decayed sums of 1, k, k^2, t, k t                       */
   uint64_t verifier_passes;      /* mtp_width_observe calls                                */
   uint64_t cycles;               /* request-cycles observed                                */
@@ -309,29 +330,38 @@ typedef struct mtp_width_ctl {
   uint64_t depth_hist[8];        /* request-cycles that kept a = 0..7 drafts               */
 } mtp_width_ctl;
 
-/* alpha[*] = alpha0 in [0, 1]; counters and sums zero.  MTP_ERR_RANGE / _SHAPE on bad
- * arguments. */
+/* A new controller (lucebox-hub PR above, "What": the adaptive width): alpha[*] = alpha0
+ * in [0, 1]; counters and sums zero.  MTP_ERR_RANGE / _SHAPE on bad arguments. */
 int mtp_width_init(mtp_width_ctl* c, int32_t k_max, double decay, double alpha0, double slope_prior);
-/* One verify pass of B requests with k drafts each: n_accept and flags are HOST copies
+/* The per-depth acceptance and the cost fit (lucebox-hub PR above, "What"), fed by one
+ * verify pass of B requests with k drafts each: n_accept and flags are HOST copies
  * of mtp_accept_sample's outputs; seconds = the pass's measured cycle time (<= 0: not
  * timed).  MTP_ERR_RANGE if some n_accept is outside [0, k]; nothing is updated then. */
 int mtp_width_observe(mtp_width_ctl* c, int32_t k, int32_t B, const int32_t* n_accept, const uint32_t* flags,
                       double seconds);
-double mtp_width_expected_tokens(const mtp_width_ctl* c, int32_t k);   /* E(k), 0 <= k <= 7   */
-double mtp_width_cost(const mtp_width_ctl* c, int32_t k);              /* c(k)                */
-int32_t mtp_width_choose(const mtp_width_ctl* c);                      /* k*, in 1..k_max     */
+/* E(k), 0 <= k <= 7: expected tokens of a k-draft cycle from the per-depth acceptance
+ * (lucebox-hub PR above, "What"). */
+double mtp_width_expected_tokens(const mtp_width_ctl* c, int32_t k);
+/* c(k): the fitted cycle cost (lucebox-hub PR above, "What": a per-request cost fit). */
+double mtp_width_cost(const mtp_width_ctl* c, int32_t k);
+/* k*, in 1..k_max: the width for the next cycle (lucebox-hub PR above, "What": up to seven
+ * drafts by default). */
+int32_t mtp_width_choose(const mtp_width_ctl* c);
 
 /* ---------------------------------------------------------------------------------- */
 /* weight preparation                                                                  */
 /* ---------------------------------------------------------------------------------- */
-/* Bytes of one array of a tiled head for a source of type wtype (MTP_W_BF16 or
+/* Build infrastructure, no passage (the pages fix the weights' arithmetic, not their
+ * layout in memory): the tiled layouts above are this library's own.
+ * Bytes of one array of a tiled head for a source of type wtype (MTP_W_BF16 or
  * MTP_W_Q4A32): part 0 = w, 1 = scale, 2 = minv (0 for a part the format lacks, or for
  * invalid arguments). */
 size_t mtp_tiled_bytes(int32_t wtype, int32_t d, int32_t vocab, int32_t part);
 
 /* Gather rows of a row-major head (F32, BF16 or Q4A32) into a new row-major head, once,
- * at load time: row r of dst = row ids[r] of src, with its scales and mins (lucebox-hub
- * PR, "What": the draft head is a subset of the vocabulary).  ids: device int32 [n],
+ * at load time: row r of dst = row ids[r] of src, with its scales and mins
+ * (lucebox-hub PR above, "What": the draft head is a subset of the vocabulary).
+ * ids: device int32 [n],
  * strictly ascending ids in [0, src->vocab) (an id outside gives a zero row); dst_* hold
  * n rows of src's formats (dst_scale and dst_minv for Q4A32 only), 16-byte aligned, not
  * overlapping src.  The result is used with row_ids = ids, directly or after
@@ -339,7 +369,8 @@ size_t mtp_tiled_bytes(int32_t wtype, int32_t d, int32_t vocab, int32_t part);
 int mtp_gather_rows(const mtp_head* src, const int32_t* ids, int32_t n, void* dst_w, void* dst_scale,
                     void* dst_minv, void* stream);
 
-/* Repack a row-major BF16 or Q4A32 head into the tiled layout (MTP_W_BF16_TILED /
+/* Build infrastructure, no passage (see mtp_tiled_bytes).
+ * Repack a row-major BF16 or Q4A32 head into the tiled layout (MTP_W_BF16_TILED /
  * MTP_W_Q4A32_TILED) on the device, once, at load time.  dst_* are device buffers of
  * mtp_tiled_bytes(src->wtype, ...) bytes (dst_scale and dst_minv only for Q4A32), 16-byte
  * aligned, not overlapping the source.  The tiled head gives the LM-head kernels the
@@ -349,8 +380,12 @@ int mtp_pack_head(const mtp_head* src, void* dst_w, void* dst_scale, void* dst_m
 /* ---------------------------------------------------------------------------------- */
 /* misc                                                                                */
 /* ---------------------------------------------------------------------------------- */
-const char* mtp_status_str(int status);   /* static string; never NULL                 */
-int mtp_abi_version(void);                /* MTP_ABI_VERSION                            */
+/* The clear message for a status code (llama.cpp PR above, loader commit): a static
+ * string, never NULL, "unknown status" for a code not listed. */
+const char* mtp_status_str(int status);
+/* Build infrastructure, no passage: MTP_ABI_VERSION, for a caller to check at load time
+ * that its copy of this header matches the library. */
+int mtp_abi_version(void);
 
 #ifdef __cplusplus
 }

@@ -34,6 +34,28 @@ def test_header_declares_the_four_calls():
     assert set(names) == set(mtp.EXPORTED)
 
 
+SOURCE_NAMES = ("lucebox-hub PR", "llama.cpp PR", "DS4Server issue", "Build infrastructure")
+
+
+def _declarations_with_comments():
+    """(name, the header text between the previous declaration's end and this one)."""
+    src = open(HEADER).read()
+    out, prev_end = [], 0
+    for m in re.finditer(r"^(?![ /*])[A-Za-z_][\w \t*]*?\b(mtp_[a-z_]+)\s*\(", src, flags=re.M):
+        out.append((m.group(1), src[prev_end:m.start()]))
+        prev_end = src.index(";", m.end())
+    return out
+
+
+def test_every_declared_call_cites_its_source():
+    """Each declaration is preceded by a comment naming the page (and section) that defines
+    the operation, or marking it as build infrastructure."""
+    decls = _declarations_with_comments()
+    assert sorted(n for n, _ in decls) == _declared()
+    for name, text in decls:
+        assert any(s in text for s in SOURCE_NAMES), f"{name}: no source named in its comment"
+
+
 def test_every_declared_symbol_is_exported(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", mtp.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -43,7 +65,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mtp_abi_version() == 2
+    assert lib.mtp_abi_version() == 3
     for code in range(-7, 1):
         s = lib.mtp_status_str(code)
         assert s and s != b"unknown status"
