@@ -200,14 +200,17 @@ int mtp_verify_logits(const mtp_head* head, const void* hidden, int32_t htype, i
   if (B < 1) return MTP_ERR_SHAPE;
   const int M = B * (k + 1);
   if (M > kLmheadMaxWideRows) return MTP_ERR_SHAPE;
-  const bool wide = M > kLmheadMaxRows;
+  // the wide kernel above 16 rows, and for every row count of a head whose 16 hidden rows
+  // do not fit the other kernel's LDS (a property of the head alone, so a row's results
+  // still do not depend on how many rows share the launch)
+  const bool wide = M > kLmheadMaxRows || lmhead_lds_bytes_for(head->wtype, head->d, kLmheadMaxRows) > kMaxLds;
   const bool sampled = smp->temperature > 0.0f;
   const bool exact = sampled && smp->accept_rule == MTP_ACCEPT_EXACT;
   if (sampled && !exact && !logits) return MTP_ERR_NULL;
   if (exact && !smp->positions) return MTP_ERR_NULL;
   if (!aligned16(hidden) || !aligned16(row_stats) || (logits && !aligned16(logits))) return MTP_ERR_ALIGN;
   if (exact && !aligned16(smp->positions)) return MTP_ERR_ALIGN;
-  if ((wide ? lmhead_wide_lds_bytes() : lmhead_lds_bytes_for(head->wtype, head->d, M)) > kMaxLds) return MTP_ERR_SHAPE;
+  if (wide && lmhead_wide_lds_bytes() > kMaxLds) return MTP_ERR_SHAPE;
   if (!ws || !aligned256(ws)) return ws ? MTP_ERR_ALIGN : MTP_ERR_WORKSPACE;
   if (ws_bytes < lmhead_ws_bytes(M, head->vocab)) return MTP_ERR_WORKSPACE;
 

@@ -57,8 +57,9 @@ __host__ __device__ inline size_t lmhead_partials_offset(int M) { return 256 + (
 size_t lmhead_ws_bytes(int M, int n_rows);
 size_t lmhead_lds_bytes_for(int wtype, int d, int M);   // LDS a launch needs
 hipError_t launch_lmhead(const LmheadLaunch& p, hipStream_t stream);
-// verify pass for kLmheadMaxRows < M <= kLmheadMaxWideRows: the wide kernel, then one
-// merge block per hidden row
+// verify pass with the wide kernel, then one merge block per hidden row: for
+// kLmheadMaxRows < M <= kLmheadMaxWideRows, and for any M when the head's hidden size leaves
+// no room for 16 staged hidden rows in the other kernel's LDS
 size_t lmhead_wide_lds_bytes();
 hipError_t launch_lmhead_wide(const LmheadLaunch& p, hipStream_t stream);
 

@@ -33,49 +33,24 @@ namespace {
 
 using namespace lm;
 
-// Tuning knobs (compile-time): tiles per wave pass, K steps per prefetch chunk, the grid
-// cap, and the waves per SIMD the register budget is sized for.
-#ifndef MTP_LM_TV
-#define MTP_LM_TV 1
-#endif
-#ifndef MTP_LM_U
-#define MTP_LM_U 8
-#endif
-#ifndef MTP_LM_TV_Q4
-#define MTP_LM_TV_Q4 2
-#endif
-#ifndef MTP_LM_U_Q4
-#define MTP_LM_U_Q4 8
-#endif
-#ifndef MTP_LM_TV_Q4_SAMPLED
-#define MTP_LM_TV_Q4_SAMPLED 1
-#endif
-#ifndef MTP_LM_MAX_GRID
-#define MTP_LM_MAX_GRID 256
-#endif
-#ifndef MTP_LM_WAVES_PER_EU
-#define MTP_LM_WAVES_PER_EU 1
-#endif
-
-#ifndef MTP_LM_WAVES
-#define MTP_LM_WAVES 8
-#endif
-constexpr int kWaves = MTP_LM_WAVES;   // waves per block
+// Launch shape (measured choices): 8 waves per block, one block per CU at most; tiles per
+// wave pass and K steps per prefetch chunk per head format.
+constexpr int kWaves = 8;            // waves per block (4, one per SIMD, was slower everywhere)
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTV = MTP_LM_TV;       // 16-row vocabulary tiles per wave per pass
-constexpr int kU = MTP_LM_U;         // K steps per prefetch chunk
-constexpr int kTVQ4 = MTP_LM_TV_Q4;  // the same for 4-bit heads, whose K steps carry a
-constexpr int kUQ4 = MTP_LM_U_Q4;    // quarter of the bytes
+constexpr int kTV = 1;               // 16-row vocabulary tiles per wave per pass
+constexpr int kU = 8;                // K steps per prefetch chunk
+constexpr int kTVQ4 = 2;             // the same for 4-bit heads, whose K steps carry a
+constexpr int kUQ4 = 8;              // quarter of the bytes
 // 4-bit heads under sampling keep the Gumbel state live through the K loop: one tile per
 // pass keeps them out of scratch (two spilled 108-156 bytes per lane and ran 9-11% slower)
-constexpr int kTVQ4S = MTP_LM_TV_Q4_SAMPLED;
+constexpr int kTVQ4S = 1;
 
 // tiles per wave pass of a launch
 template <int WT, bool SAMPLED>
 constexpr int tiles_per_pass() {
   return Layout<WT>::q4 ? (SAMPLED ? kTVQ4S : kTVQ4) : kTV;
 }
-constexpr int kMaxGrid = MTP_LM_MAX_GRID;
+constexpr int kMaxGrid = 256;        // blocks per launch (partials per row in the workspace)
 
 // Quad broadcast on the DPP network: every lane of each group of 4 reads lane R's value.
 template <int R>
@@ -475,13 +450,13 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
 }  // namespace
 
 template <int WT, bool SAMPLED, int RL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MTP_LM_WAVES_PER_EU)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void mtp_draft_head_kernel(LmheadLaunch p) {
   lmhead_body<WT, SAMPLED, false, RL>(p);
 }
 
 template <int WT, bool SAMPLED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MTP_LM_WAVES_PER_EU)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void mtp_verify_logits_kernel(LmheadLaunch p) {
   lmhead_body<WT, SAMPLED, true, 4>(p);
 }

@@ -1,7 +1,8 @@
 // Verify pass for 17..128 hidden rows (several requests' k+1 verify rows in one launch):
 // the verify of lucebox-hub PR "feat(qwen4exp): MTP speculative decoding", section "What"
 // (every draft of a request checked by one batched forward of the full head), batched over
-// requests.
+// requests.  It also takes every verify of a head whose hidden size is too large for the
+// other kernel to stage 16 hidden rows in LDS (its own LDS use does not depend on d).
 //
 // The mapping is the one of the kernel for up to 16 rows (weights are the MFMA B operand,
 // streamed once, tile by tile; every logit is one accumulator chain over K in a fixed
@@ -27,24 +28,9 @@ namespace {
 using namespace lm;
 
 constexpr int kWaves = kLmheadThreads / 64;   // 8
-#ifndef MTP_WIDE_TV
-#define MTP_WIDE_TV 2
-#endif
-#ifndef MTP_WIDE_U
-#define MTP_WIDE_U 4
-#endif
-#ifndef MTP_WIDE_SKIP_IDLE
-#define MTP_WIDE_SKIP_IDLE 0
-#endif
-#ifndef MTP_WIDE_GRID
-#define MTP_WIDE_GRID 0
-#endif
-constexpr int WTV = MTP_WIDE_TV;              // tiles a wave works on at once
-constexpr int WU = MTP_WIDE_U;                // K steps per staged chunk
-#ifndef MTP_WIDE_NB
-#define MTP_WIDE_NB 2
-#endif
-constexpr int NB = MTP_WIDE_NB;               // weight chunks in registers (NB-1 in flight)
+constexpr int WTV = 2;                        // tiles a wave works on at once
+constexpr int WU = 4;                         // K steps per staged chunk
+constexpr int NB = 2;                         // weight chunks in registers (NB-1 in flight)
 constexpr int NCB = 8;                        // column blocks of 16 hidden rows
 constexpr int kRows = NCB * 16;               // 128
 constexpr int kFragsPerChunk = WU * NCB * 64; // 16-byte A fragments per chunk
@@ -711,12 +697,11 @@ __device__ __forceinline__ void wide_body(const LmheadLaunch& p) {
   stage_load(S, 1 % nch);
   __syncthreads();
   int it = 0;
-  bool busy = true;
   auto step = [&](Chunk& cur, Chunk& ahead, int ch) {
     load(ahead, it + NB - 1);
     // the next chunk's hidden fragments go to LDS between the two halves of this chunk's
     // MFMAs, so that the LDS writes overlap the second half
-    const bool act = busy && ch * WU < nsteps;
+    const bool act = ch * WU < nsteps;
     if (act) comp(cur, ch, it & 1, std::integral_constant<int, 0>{}, std::integral_constant<int, WU / 2>{});
     stage_store(S, (it + 1) & 1);
     if (act) comp(cur, ch, it & 1, std::integral_constant<int, WU / 2>{}, std::integral_constant<int, WU>{});
@@ -726,7 +711,6 @@ __device__ __forceinline__ void wide_body(const LmheadLaunch& p) {
   };
   for (int pass = 0; pass < npass; ++pass) {
     zero_acc();
-    busy = !MTP_WIDE_SKIP_IDLE || t_begin + pass * WTV < t_end;   // wave-uniform
     for (int ch = 0; ch < nch; ch += NB) {
 #pragma unroll
       for (int k = 0; k < NB; ++k) step(Wb[k], Wb[(k + NB - 1) % NB], ch + k);
@@ -824,7 +808,7 @@ static int wide_grid(int n_rows) {
 
 template <int WT, bool SAMPLED>
 static hipError_t launch_wide_t(const LmheadLaunch& p, hipStream_t stream) {
-  const int G = MTP_WIDE_GRID > 0 ? min(MTP_WIDE_GRID, lmhead_grid(p.n_rows)) : wide_grid(p.n_rows);
+  const int G = wide_grid(p.n_rows);
   const size_t lds = lmhead_wide_lds_bytes();
   auto kern = mtp_verify_wide_kernel<WT, SAMPLED>;
   if (lds > 65536) {
@@ -840,7 +824,7 @@ static hipError_t launch_wide_t(const LmheadLaunch& p, hipStream_t stream) {
 }
 
 hipError_t launch_lmhead_wide(const LmheadLaunch& p, hipStream_t stream) {
-  if (p.M <= kLmheadMaxRows || p.M > kLmheadMaxWideRows || !p.verify) return hipErrorInvalidValue;
+  if (p.M < 1 || p.M > kLmheadMaxWideRows || !p.verify) return hipErrorInvalidValue;
   switch (p.wtype) {
     case MTP_W_F32: return p.sampled ? launch_wide_t<MTP_W_F32, true>(p, stream) : launch_wide_t<MTP_W_F32, false>(p, stream);
     case MTP_W_BF16: return p.sampled ? launch_wide_t<MTP_W_BF16, true>(p, stream) : launch_wide_t<MTP_W_BF16, false>(p, stream);

@@ -211,3 +211,27 @@ def test_batched_model_cycle_and_commit(T):
     assert np.array_equal(live.cpu().numpy(), want_live)
     assert np.array_equal(kv.cpu().numpy(), want_kv)
     assert np.array_equal(kv_len.cpu().numpy(), want_len)
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_large_hidden_size_verify_takes_the_wide_kernel(T):
+    """d = 5120: 16 staged bf16 hidden rows (160 KiB) do not fit the 16-row kernel's LDS, so
+    every verify of this head, at any row count, runs the wide kernel: whole cycles against
+    the oracle at 16 and 8 verify rows, and request 0's logits and statistics identical
+    across the two launch sizes."""
+    V, d, nd, k = 1013, 5120, 400, 7
+    head, hv, hd, htype, depths = _planted_case("bf16", V, d, nd, 2, k, seed=91)
+    dh = dev_head(head)
+    outs = []
+    for B in (2, 1):
+        o = _oracle_cycle(head, nd, hv[:B], hd[:B], htype, T, 77, 3, 2e-2)
+        gc = GpuCycle(dh, nd, B, k, T, seed=77)
+        g = gc.run(dev_hidden(np.ascontiguousarray(hd[:B])), dev_hidden(np.ascontiguousarray(hv[:B])), cycle=3)
+        check_cycle(g, o, T, 2e-2, tag=f"d5120 B{B} T{T}")
+        if T == 0:
+            assert list(g["n_accept"]) == depths[:B]
+        outs.append((gc.row_stats.cpu().numpy(), None if gc.logits is None else gc.logits.cpu().numpy()))
+    st2, st1 = outs[0][0][0], outs[1][0][0]
+    assert np.array_equal(st1[:, [0, 1, 3, 5, 6]], st2[:, [0, 1, 3, 5, 6]])
+    if T > 0:
+        assert np.array_equal(outs[0][1][0].view(np.uint32), outs[1][1][0].view(np.uint32))
