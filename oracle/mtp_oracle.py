@@ -85,6 +85,7 @@ ACC_ROW_INVALID = 1 << 3
 ACC_NONFINITE_TARGET = 1 << 4
 ACC_NONFINITE_DRAFT = 1 << 5
 ACC_DRAFT_INVALID = 1 << 6
+ACC_EOS_DRAFT = 1 << 7   # the block ended on an accepted EOS draft (not a correction/bonus EOS)
 
 STREAM_DRAFT, STREAM_ACCEPT, STREAM_RESAMPLE, STREAM_TRUNK = 0, 1, 2, 3
 RULE_RATIO, RULE_EXACT = "ratio", "exact"
@@ -601,6 +602,7 @@ def accept(drafts, zd_raw, zv_raw, n_draft: int, T: float, seed: int, cycle: int
             last[sel] = y[sel, k]
             mark_tie(np.isin(rows, sel[gap_near_tie(y_margin[sel, k], delta)]), k)
     flags[stop_kind == 3] |= ACC_ROW_INVALID
+    flags[stop_kind == 1] |= ACC_EOS_DRAFT
 
     # emitted block: the accepted drafts, then the correction / bonus / EOS token
     col = np.arange(k + 1)[None, :]

@@ -261,6 +261,7 @@ __global__ __launch_bounds__(kAcceptThreads) void mtp_accept_sample_kernel(Accep
   }
   if (c.kind == kAllAccepted) c.flags |= MTP_ACC_ALL_ACCEPTED;
   if (c.kind == kInvalidRow) c.flags |= MTP_ACC_ROW_INVALID;
+  if (c.kind == kEosDraft) c.flags |= MTP_ACC_EOS_DRAFT;
   const bool has_last = c.kind != kInvalidRow;
   if (has_last && p.eos >= 0 && c.last == p.eos) c.flags |= MTP_ACC_EOS;
   int32_t* out = p.out_tokens + (size_t)b * K1;

@@ -5,6 +5,11 @@
 // The controller is a plain struct the caller owns, one per request stream; it is fed
 // the acceptance outputs of each cycle (copied to the host) and the cycle's measured
 // time, and it proposes the next width.  Arithmetic in double, in a fixed order.
+//
+// Exploration: a depth decided too rarely to be current (recency weight below 1/2) is
+// estimated by the depth before it.  Acceptance seldom rises with depth, so depths the
+// current width never reaches get an optimistic estimate, and a rise in acceptance at the
+// shallow depths makes the controller try deeper drafts, which then measure their own rate.
 #include <cmath>
 
 #include "../../include/mtp.h"
@@ -22,6 +27,7 @@ int mtp_width_init(mtp_width_ctl* c, int32_t k_max, double decay, double alpha0,
   c->decay = decay;
   c->slope_prior = slope_prior;
   for (double& a : c->alpha) a = alpha0;
+  for (double& w : c->weight) w = 0.0;
   return MTP_OK;
 }
 
@@ -40,11 +46,19 @@ int mtp_width_observe(mtp_width_ctl* c, int32_t k, int32_t B, const int32_t* n_a
     c->drafted += (uint64_t)k;
     c->accepted += (uint64_t)a;
     c->depth_hist[a] += 1;
-    for (int j = 0; j < a; ++j) c->alpha[j] += lam * (1.0 - c->alpha[j]);   // drafts 1..a accepted
-    // a rejection at draft a+1; an EOS end, an unusable target row or a full accept say
-    // nothing about it
-    if (a < k && !(f & (MTP_ACC_EOS | MTP_ACC_ROW_INVALID | MTP_ACC_ALL_ACCEPTED)))
+    for (double& w : c->weight) w = (1.0 - lam) * w;
+    // an accepted EOS draft is draft a+1, accepted
+    const int accepted = (a < k && (f & MTP_ACC_EOS_DRAFT)) ? a + 1 : a;
+    for (int j = 0; j < accepted; ++j) {   // drafts 1..accepted
+      c->alpha[j] += lam * (1.0 - c->alpha[j]);
+      c->weight[j] += 1.0;
+    }
+    // a rejection at draft a+1 (an EOS correction included); an unusable target row or a
+    // full accept say nothing about it
+    if (accepted == a && a < k && !(f & (MTP_ACC_ROW_INVALID | MTP_ACC_ALL_ACCEPTED))) {
       c->alpha[a] += lam * (0.0 - c->alpha[a]);
+      c->weight[a] += 1.0;
+    }
   }
   if (seconds > 0.0 && std::isfinite(seconds)) {
     const double g = 1.0 - lam;
@@ -85,9 +99,11 @@ double mtp_width_cost(const mtp_width_ctl* c, int32_t k) {
 
 double mtp_width_expected_tokens(const mtp_width_ctl* c, int32_t k) {
   if (!c || k < 0 || k > 7) return NAN;
-  double e = 1.0, run = 1.0;
+  constexpr double kStaleWeight = 0.5;
+  double e = 1.0, run = 1.0, est = c->alpha[0];
   for (int j = 0; j < k; ++j) {
-    run *= c->alpha[j];
+    if (j > 0 && c->weight[j] >= kStaleWeight) est = c->alpha[j];   // else: depth j-1's estimate
+    run *= est;
     e += run;
   }
   return e;

@@ -25,7 +25,7 @@ H_F32, H_BF16 = 0, 1
 OP_DRAFT, OP_VERIFY, OP_ACCEPT = 0, 1, 2
 ROW_NONFINITE, ROW_POSINF, ROW_INVALID = 0x1, 0x2, 0x4
 ACC_ALL_ACCEPTED, ACC_EOS, ACC_RESID_FALLBACK, ACC_ROW_INVALID = 0x01, 0x02, 0x04, 0x08
-ACC_NONFINITE_TARGET, ACC_NONFINITE_DRAFT, ACC_DRAFT_INVALID = 0x10, 0x20, 0x40
+ACC_NONFINITE_TARGET, ACC_NONFINITE_DRAFT, ACC_DRAFT_INVALID, ACC_EOS_DRAFT = 0x10, 0x20, 0x40, 0x80
 ROW_STATS_WORDS = 8   # sizeof(mtp_row_stats) / 4
 ACCEPT_RATIO, ACCEPT_EXACT = 0, 1
 
@@ -41,7 +41,8 @@ class MtpError(RuntimeError):
 
 class _WidthCtl(ctypes.Structure):
     _fields_ = [("k_max", ctypes.c_int32), ("reserved", ctypes.c_int32), ("decay", ctypes.c_double),
-                ("slope_prior", ctypes.c_double), ("alpha", ctypes.c_double * 7), ("sw", ctypes.c_double),
+                ("slope_prior", ctypes.c_double), ("alpha", ctypes.c_double * 7),
+                ("weight", ctypes.c_double * 7), ("sw", ctypes.c_double),
                 ("sk", ctypes.c_double), ("skk", ctypes.c_double), ("st", ctypes.c_double), ("skt", ctypes.c_double),
                 ("verifier_passes", ctypes.c_uint64), ("cycles", ctypes.c_uint64), ("drafted", ctypes.c_uint64),
                 ("accepted", ctypes.c_uint64), ("depth_hist", ctypes.c_uint64 * 8)]
@@ -328,6 +329,10 @@ class WidthController:
     @property
     def alpha(self):
         return list(self._c.alpha)
+
+    @property
+    def weight(self):
+        return list(self._c.weight)
 
     @property
     def counters(self) -> dict:
