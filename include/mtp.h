@@ -290,6 +290,22 @@ int mtp_commit_state(int32_t B, int32_t k, const int32_t* n_accept, const void* 
                      void* live, size_t state_bytes, void* kv, int32_t n_layers,
                      int32_t max_rows, size_t kv_row_bytes, int32_t* kv_len, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving
+ * loops or harnesses that forbid hipMalloc): mtp_verify_logits without a workspace.  The
+ * scratch the verify kernels need lives in a device array inside the library, 1,573,632
+ * bytes per GPU (enough for any valid call: up to 128 rows, any vocabulary), held until
+ * the process ends; its address is resolved, and its completion ticket cleared, on the
+ * first call on each device.  The call allocates nothing.  Results are those of
+ * mtp_verify_logits, bit for bit.  All calls on one GPU share the array and each leaves
+ * it ready for the next: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.  MTP_ERR_WORKSPACE if a call would
+ * need more scratch than the array holds; otherwise the same status codes as
+ * mtp_verify_logits. */
+int mtp_verify_logits_noalloc(const mtp_head* head, const void* hidden, int32_t htype, int32_t B,
+                              int32_t k, const int32_t* draft_tokens, int32_t k_max,
+                              const mtp_sampling* smp, mtp_row_stats* row_stats, float* logits,
+                              void* stream);
+
 /* ---------------------------------------------------------------------------------- */
 /* adaptive verify width (host side)                                                   */
 /* ---------------------------------------------------------------------------------- */

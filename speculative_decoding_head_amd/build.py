@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmtp.so")
-SOURCES = ["api.cpp", "lmhead.hip", "lmhead_wide.hip", "accept.hip", "commit.hip", "pack.hip", "width.cpp"]
+SOURCES = ["api.cpp", "lmhead.hip", "lmhead_wide.hip", "accept.hip", "commit.hip", "pack.hip", "width.cpp",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -191,6 +191,18 @@ int mtp_verify_logits(const mtp_head* head, const void* hidden, int32_t htype, i
                       int32_t k, const int32_t* draft_tokens, int32_t k_max,
                       const mtp_sampling* smp, mtp_row_stats* row_stats, float* logits,
                       void* ws, size_t ws_bytes, void* stream) {
+  VerifyPlan plan;
+  const int st = verify_logits_prepare(head, hidden, htype, B, k, draft_tokens, k_max, smp, row_stats, logits, &plan);
+  return st != MTP_OK ? st : verify_logits_run(plan, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace mtp {
+
+int verify_logits_prepare(const mtp_head* head, const void* hidden, int32_t htype, int32_t B, int32_t k,
+                          const int32_t* draft_tokens, int32_t k_max, const mtp_sampling* smp,
+                          mtp_row_stats* row_stats, float* logits, VerifyPlan* plan) {
   int st = check_head(head, htype);
   if (st != MTP_OK) return st;
   if ((st = check_sampling(smp)) != MTP_OK) return st;
@@ -211,10 +223,9 @@ int mtp_verify_logits(const mtp_head* head, const void* hidden, int32_t htype, i
   if (!aligned16(hidden) || !aligned16(row_stats) || (logits && !aligned16(logits))) return MTP_ERR_ALIGN;
   if (exact && !aligned16(smp->positions)) return MTP_ERR_ALIGN;
   if (wide && lmhead_wide_lds_bytes() > kMaxLds) return MTP_ERR_SHAPE;
-  if (!ws || !aligned256(ws)) return ws ? MTP_ERR_ALIGN : MTP_ERR_WORKSPACE;
-  if (ws_bytes < lmhead_ws_bytes(M, head->vocab)) return MTP_ERR_WORKSPACE;
 
-  LmheadLaunch p{};
+  LmheadLaunch& p = plan->p;
+  p = LmheadLaunch{};
   p.wtype = head->wtype;
   p.w = head->w;
   p.scale = static_cast<const uint16_t*>(head->scale);
@@ -245,11 +256,24 @@ int mtp_verify_logits(const mtp_head* head, const void* hidden, int32_t htype, i
   p.out_offset = 0;
   p.logits = logits;
   p.logits_stride = head->vocab;
-  p.ws = ws;
-  const hipError_t e = wide ? launch_lmhead_wide(p, static_cast<hipStream_t>(stream))
-                            : launch_lmhead(p, static_cast<hipStream_t>(stream));
+  p.ws = nullptr;
+  plan->wide = wide;
+  plan->ws_need = lmhead_ws_bytes(M, head->vocab);
+  return MTP_OK;
+}
+
+int verify_logits_run(VerifyPlan& plan, void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || !aligned256(ws)) return ws ? MTP_ERR_ALIGN : MTP_ERR_WORKSPACE;
+  if (ws_bytes < plan.ws_need) return MTP_ERR_WORKSPACE;
+  plan.p.ws = ws;
+  const hipError_t e = plan.wide ? launch_lmhead_wide(plan.p, static_cast<hipStream_t>(stream))
+                                 : launch_lmhead(plan.p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MTP_OK : MTP_ERR_HIP;
 }
+
+}  // namespace mtp
+
+extern "C" {
 
 int mtp_accept_sample(int32_t B, int32_t k, int32_t k_max, int32_t vocab, int32_t n_draft,
                       const mtp_sampling* smp, const int32_t* draft_tokens,

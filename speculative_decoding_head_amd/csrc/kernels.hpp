@@ -99,6 +99,19 @@ struct CommitLaunch {
 
 hipError_t launch_commit(const CommitLaunch& p, hipStream_t stream);
 
+// mtp_verify_logits in two steps, shared by the entry point that takes a caller's workspace
+// and the one that uses the library's own scratch: prepare validates every argument but the
+// workspace and fills the launch (no device call); run checks the workspace and launches.
+struct VerifyPlan {
+  LmheadLaunch p;
+  bool wide;
+  size_t ws_need;   // workspace bytes the launch needs
+};
+int verify_logits_prepare(const mtp_head* head, const void* hidden, int32_t htype, int32_t B, int32_t k,
+                          const int32_t* draft_tokens, int32_t k_max, const mtp_sampling* smp,
+                          mtp_row_stats* row_stats, float* logits, VerifyPlan* plan);
+int verify_logits_run(VerifyPlan& plan, void* ws, size_t ws_bytes, void* stream);
+
 size_t tiled_bytes(int wtype, int d, int vocab, int part);   // source wtype BF16 or Q4A32
 hipError_t launch_gather(int wtype, const void* w, const void* scale, const void* minv, int d, int vocab,
                          const int32_t* ids, int n, void* dst_w, void* dst_scale, void* dst_minv, hipStream_t stream);

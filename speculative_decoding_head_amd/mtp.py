@@ -32,7 +32,7 @@ ACCEPT_RATIO, ACCEPT_EXACT = 0, 1
 EXPORTED = ("mtp_draft_head", "mtp_verify_logits", "mtp_accept_sample", "mtp_commit_state",
             "mtp_workspace_bytes", "mtp_tiled_bytes", "mtp_pack_head", "mtp_status_str", "mtp_abi_version",
             "mtp_width_init", "mtp_width_observe", "mtp_width_expected_tokens", "mtp_width_cost",
-            "mtp_width_choose", "mtp_gather_rows")
+            "mtp_width_choose", "mtp_gather_rows", "mtp_verify_logits_noalloc")
 
 
 class MtpError(RuntimeError):
@@ -75,11 +75,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     hp, sp = ctypes.POINTER(_Head), ctypes.POINTER(_Sampling)
     lib.mtp_draft_head.argtypes = [hp, i32, vp, i32, i32, i32, i32, sp, vp, vp, vp, vp, sz, vp]
     lib.mtp_verify_logits.argtypes = [hp, vp, i32, i32, i32, vp, i32, sp, vp, vp, vp, sz, vp]
+    lib.mtp_verify_logits_noalloc.argtypes = [hp, vp, i32, i32, i32, vp, i32, sp, vp, vp, vp]
     lib.mtp_accept_sample.argtypes = [i32, i32, i32, i32, i32, sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.mtp_gather_rows.argtypes = [hp, vp, i32, vp, vp, vp, vp]
     lib.mtp_gather_rows.restype = ctypes.c_int
     lib.mtp_commit_state.argtypes = [i32, i32, vp, vp, vp, sz, vp, i32, i32, sz, vp, vp]
-    for f in ("mtp_draft_head", "mtp_verify_logits", "mtp_accept_sample", "mtp_commit_state", "mtp_abi_version"):
+    for f in ("mtp_draft_head", "mtp_verify_logits", "mtp_verify_logits_noalloc", "mtp_accept_sample",
+              "mtp_commit_state", "mtp_abi_version"):
         getattr(lib, f).restype = ctypes.c_int
     lib.mtp_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.mtp_workspace_bytes.restype = sz
@@ -265,6 +267,20 @@ def mtp_verify_logits(head: Head, hidden: torch.Tensor, k: int, draft_tokens: to
                                  _ptr(row_stats, (torch.int32,), "row_stats"),
                                  _ptr(logits, (torch.float32,), "logits"),
                                  _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def mtp_verify_logits_noalloc(head: Head, hidden: torch.Tensor, k: int, draft_tokens: torch.Tensor, k_max: int,
+                              smp: _Sampling, row_stats: torch.Tensor, logits: Optional[torch.Tensor],
+                              stream=None) -> None:
+    """mtp_verify_logits on the library's own per-device scratch: no workspace argument,
+    nothing allocated (calls on one GPU must not overlap)."""
+    lib = load_library()
+    B = hidden.shape[0] if hidden.dim() == 3 else hidden.shape[0] // (k + 1)
+    h = head._struct()
+    _check(lib.mtp_verify_logits_noalloc(ctypes.byref(h), _ptr(hidden, name="hidden"), _htype(hidden), int(B),
+                                         int(k), _ptr(draft_tokens, (torch.int32,), "draft_tokens"), int(k_max),
+                                         ctypes.byref(smp), _ptr(row_stats, (torch.int32,), "row_stats"),
+                                         _ptr(logits, (torch.float32,), "logits"), _stream(stream)))
 
 
 def mtp_accept_sample(B: int, k: int, k_max: int, vocab: int, n_draft: int, smp: _Sampling,

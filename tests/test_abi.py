@@ -34,7 +34,9 @@ def test_header_declares_the_four_calls():
     assert set(names) == set(mtp.EXPORTED)
 
 
-SOURCE_NAMES = ("lucebox-hub PR", "llama.cpp PR", "DS4Server issue", "Build infrastructure")
+# the pages, build infrastructure, or (the allocation-free variant of a call) the callers it is for
+SOURCE_NAMES = ("lucebox-hub PR", "llama.cpp PR", "DS4Server issue", "Build infrastructure",
+                "callers that cannot allocate")
 
 
 def _declarations_with_comments():
@@ -49,7 +51,7 @@ def _declarations_with_comments():
 
 def test_every_declared_call_cites_its_source():
     """Each declaration is preceded by a comment naming the page (and section) that defines
-    the operation, or marking it as build infrastructure."""
+    the operation, marking it as build infrastructure, or naming the callers it is for."""
     decls = _declarations_with_comments()
     assert sorted(n for n, _ in decls) == _declared()
     for name, text in decls:

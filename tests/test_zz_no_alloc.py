@@ -1,0 +1,91 @@
+"""The allocation-free verify entry point (mtp_verify_logits_noalloc, for callers that cannot
+allocate device memory) against mtp_verify_logits with a caller's workspace: two calls in a
+row on the library's per-device scratch, the second smaller than the first (a 128-row wide
+launch with sampled logits, then a 4-row launch of the 16-row kernel at T = 0), and a third
+at the first size again; row statistics and logits identical bit for bit.  Argument checks
+run before any device call."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import speculative_decoding_head_amd as mtp
+import synth
+from gpu_cycle import dev_head, dev_hidden
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-case] {request.node.nodeid}", flush=True)
+    yield
+    if torch.cuda.is_available():
+        torch.cuda.synchronize()
+
+
+def _inputs(rng, head, B, k, d, V):
+    h_v, _ = synth.make_hidden(rng, B, k, d)
+    hv = dev_hidden(synth.encode_hidden(h_v, "bf16"))
+    drafts = torch.from_numpy(rng.integers(0, V, size=(B, 7)).astype(np.int32)).cuda()
+    return hv, drafts
+
+
+def _both(dh, hv, drafts, B, k, T, V):
+    smp = mtp.sampling(T, -1, 4321, 7, 0)
+    out = []
+    for noalloc in (False, True):
+        st = mtp.row_stats_empty(B, k + 1)
+        lg = torch.full((B, k + 1, V), 7.0, dtype=torch.float32, device="cuda") if T > 0 else None
+        if noalloc:
+            mtp.mtp_verify_logits_noalloc(dh, hv, k, drafts, 7, smp, st, lg)
+        else:
+            ws = mtp.workspace(mtp.workspace_bytes(mtp.OP_VERIFY, B * (k + 1), V, B))
+            mtp.mtp_verify_logits(dh, hv, k, drafts, 7, smp, st, lg, ws)
+        torch.cuda.synchronize()
+        out.append((st.cpu().numpy(), None if lg is None else lg.cpu().numpy()))
+    return out
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("tiled", [False, True])
+def test_noalloc_verify_equals_the_workspace_verify(tiled):
+    V, d = 4099, 256
+    rng = np.random.default_rng(17)
+    head = synth.make_head(rng, V, d, "bf16")
+    dh = dev_head(head, tiled=tiled)
+    for B, k, T in ((16, 7, 1.0), (1, 3, 0.0), (16, 7, 1.0)):
+        hv, drafts = _inputs(rng, head, B, k, d, V)
+        (st_ws, lg_ws), (st_na, lg_na) = _both(dh, hv, drafts, B, k, T, V)
+        assert np.array_equal(st_ws, st_na), (B, k, T)
+        if T > 0:
+            assert np.array_equal(lg_ws.view(np.uint32), lg_na.view(np.uint32)), (B, k, T)
+        assert np.all(st_na.reshape(-1, 8)[:, 3] >= 0)          # every row has an argmax
+
+
+@pytest.mark.gpu
+def test_noalloc_verify_at_model_scale():
+    """The model-scale verify (152,064 x 2560 bf16, tiled, 8 rows) on the scratch array."""
+    wl = synth.WORKLOADS["model_greedy"]
+    rng = np.random.default_rng(wl.seed)
+    head = synth.make_head(rng, wl.V, wl.d, wl.wtype)
+    dh = dev_head(head, tiled=True)
+    hv, drafts = _inputs(rng, head, 1, wl.k, wl.d, wl.V)
+    (st_ws, _), (st_na, _) = _both(dh, hv, drafts, 1, wl.k, 0.0, wl.V)
+    assert np.array_equal(st_ws, st_na)
+
+
+def test_noalloc_rejects_bad_arguments_before_touching_a_device():
+    if not __import__("os").path.exists(mtp.LIB_PATH):
+        pytest.skip("libmtp.so not built")
+    if torch.cuda.is_available():
+        pytest.skip("checks with fake pointers run on CPU-only hosts")
+    lib = mtp.load_library()
+    FAKE = 0x10000
+    h = mtp.mtp._Head(mtp.W_BF16, 256, 1024, 0, FAKE, None, None, None)
+    smp = mtp.sampling(0.0, -1, 0, 0, 0)
+    args = lambda B, k, hd=FAKE: (ctypes.byref(h), hd, mtp.H_BF16, B, k, FAKE, 7, ctypes.byref(smp), FAKE, None, None)
+    assert lib.mtp_verify_logits_noalloc(*args(17, 7)) == -2          # 136 rows: more than one launch takes
+    assert lib.mtp_verify_logits_noalloc(*args(1, 8)) == -2           # k > 7
+    assert lib.mtp_verify_logits_noalloc(*args(1, 3, None)) == -1     # no hidden rows
+    assert lib.mtp_verify_logits_noalloc(None, FAKE, mtp.H_BF16, 1, 3, FAKE, 7, ctypes.byref(smp), FAKE,
+                                         None, None) == -1
