@@ -62,15 +62,17 @@ def parse():
                          "spread of their rates (value stays the first window)")
     ap.add_argument("--adaptive-cycles", type=int, default=200,
                     help="after the planted-acceptance cycles (one request only), run this many cycles whose "
-                         "width the native controller picks, and as many at the full width, both synchronising "
-                         "every cycle; 0 = skip")
+                         "width the native controller picks, and as many at each fixed width 1..k, all "
+                         "synchronising every cycle; 0 = skip")
     ap.add_argument("--draft-ids", type=int, default=0, metavar="N_TOP",
                     help="draft from an id list instead of the first n_draft ids: the N_TOP highest ids (a "
                          "special-token block at the end of the vocabulary) plus the lowest ones, n_draft in all, "
                          "gathered once into their own head; 0 = the first n_draft ids")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-commit", action="store_true", help="leave the commit out of the step")
-    ap.add_argument("--no-copy-peak", action="store_true", help="skip the 1 GiB copy-peak measurement")
+    ap.add_argument("--no-read-peak", action="store_true", help="skip the 1 GiB read-ceiling measurement")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="model_greedy only: skip timing the 16 x 8-row batched cycle and the 4-bit head cycle")
     ap.add_argument("--row-major", action="store_true",
                     help="keep the head row-major instead of repacking it once into the tiled layout")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -281,7 +283,7 @@ def main():
         live = torch.zeros(B, state_bytes, dtype=torch.uint8, device=dev)
         # room for every cycle's accepted rows, so the trim never saturates at the cache end
         kv_rows = KV_ROWS + (k + 1) * (args.warmup + args.steps * (1 + args.repeats) + 16 + args.extra_cycles
-                                       + 2 * args.adaptive_cycles)
+                                       + (k + 1) * args.adaptive_cycles)
         kv = torch.zeros(B, KV_LAYERS, 2, kv_rows, kv_row_bytes, dtype=torch.uint8, device=dev)
         kv_len = torch.zeros(B, dtype=torch.int32, device=dev)
     # the position verify row 0 predicts: the committed length (exact-match rule)
@@ -526,15 +528,15 @@ def main():
                     mtp.mtp_commit_state(B, kk, nacc, snaps[:, :kk + 1], live, state_bytes, kv, KV_LAYERS, kv_rows,
                                          kv_row_bytes, kv_len, stream)
 
-            aw = {"alpha": args.planted_alpha, "cycles": args.adaptive_cycles}
+            aw = {"alpha": args.planted_alpha, "cycles": args.adaptive_cycles, "fixed": {}}
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            for mode in ("adaptive", "full_width"):
+            for mode in ["adaptive"] + list(range(1, k + 1)):
                 ctl = mtp.WidthController(k_max=k)
                 hist, toks, dev_s = [0] * (k + 1), 0, 0.0
                 torch.cuda.synchronize()
                 t1 = time.perf_counter()
                 for c in range(args.adaptive_cycles):
-                    kk = ctl.choose() if mode == "adaptive" else k
+                    kk = ctl.choose() if mode == "adaptive" else mode
                     e0.record(stream)
                     run_width(kk, c, sets[c % n_sets])
                     e1.record(stream)
@@ -545,48 +547,250 @@ def main():
                     hist[kk] += 1
                     dev_s += sec
                 el = time.perf_counter() - t1
-                aw[mode] = {"tokens_per_s": round(toks / el, 1), "tokens_per_device_s": round(toks / dev_s, 1),
-                            "mean_tokens_per_cycle": round(toks / args.adaptive_cycles, 3),
-                            "width_histogram": {str(w): n for w, n in enumerate(hist) if n}}
+                entry = {"tokens_per_s": round(toks / el, 1), "tokens_per_device_s": round(toks / dev_s, 1),
+                         "mean_tokens_per_cycle": round(toks / args.adaptive_cycles, 3)}
                 if mode == "adaptive":
-                    aw[mode].update({"final_width": ctl.choose(),
-                                     "acceptance_by_depth": [round(a, 3) for a in ctl.alpha[:k]],
-                                     "cost_fit_us": {"c0": round(ctl.cost(0) * 1e6, 1),
-                                                     "c1": round((ctl.cost(1) - ctl.cost(0)) * 1e6, 1)}})
+                    entry.update({"width_histogram": {str(w): n for w, n in enumerate(hist) if n},
+                                  "final_width": ctl.choose(),
+                                  "acceptance_by_depth": [round(a, 3) for a in ctl.alpha[:k]],
+                                  "cost_fit_us": {"c0": round(ctl.cost(0) * 1e6, 1),
+                                                  "c1": round((ctl.cost(1) - ctl.cost(0)) * 1e6, 1)}})
+                    aw["adaptive"] = entry
+                else:
+                    aw["fixed"][str(mode)] = entry
+            best_w = max(aw["fixed"], key=lambda w: aw["fixed"][w]["tokens_per_device_s"])
+            aw["full_width"] = aw["fixed"][str(k)]
+            aw["best_fixed"] = {"width": int(best_w), "tokens_per_device_s": aw["fixed"][best_w]["tokens_per_device_s"]}
+            aw["adaptive_over_best_fixed"] = round(aw["adaptive"]["tokens_per_device_s"]
+                                                   / aw["fixed"][best_w]["tokens_per_device_s"], 4)
             result["adaptive_width"] = aw
 
-    # ---- measured copy peak: the library's own copy (the commit kernel) of a 512 MiB state,
-    #      best of 5, (read + write bytes) / time; the LM-head kernels' rates as a fraction of
-    #      it (torch's copy kernel reaches less: it is no ceiling for these kernels) ---------
-    if not args.no_copy_peak:
-        half = COPY_BYTES // 2
-        csnap = torch.empty(1, 2, half, dtype=torch.uint8, device=dev)
-        csnap.fill_(1)
-        clive = torch.empty(1, half, dtype=torch.uint8, device=dev)
-        cacc = torch.zeros(1, dtype=torch.int32, device=dev)
-        clen = torch.zeros(1, dtype=torch.int32, device=dev)
-        mtp.mtp_commit_state(1, 1, cacc, csnap, clive, half, None, 0, 0, 0, clen, stream)
-        torch.cuda.synchronize()
-        best = None
-        for _ in range(5):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            mtp.mtp_commit_state(1, 1, cacc, csnap, clive, half, None, 0, 0, 0, clen, stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) * 1e-3
-            best = t if best is None else min(best, t)
-        peak = 2 * half / best / 1e9
-        del csnap, clive
-        result["copy_peak"] = {"GBps": round(peak, 1),
-                               "kind": "mtp_commit_state copy of a 512 MiB state, (read + write) / time, best of 5"}
+    # ---- the other model-scale configurations, timed in the same run (not part of `value`):
+    #      the 128-row verify + commit of 16 requests, and the 4-bit head ----------------
+    if args.workload == "model_greedy" and not args.no_extra_configs and not args.row_major:
+        result["configs"] = {}
+        result["configs"]["batched_16x8"] = bench_batched(torch, mtp, synth, dh, nd, stream, args.extra_cycles,
+                                                          every, state_bytes, kv_row_bytes)
+        torch.cuda.empty_cache()
+        result["configs"]["q4_greedy"] = bench_q4(torch, mtp, synth, stream, args.extra_cycles, every, state_bytes,
+                                                  kv_row_bytes)
+        torch.cuda.empty_cache()
+
+    # ---- measured read ceiling: the library's streaming probe (the LM-head kernels' 1 KiB
+    #      per wave non-temporal loads, no arithmetic) over 1 GiB, best launch shape ----------
+    if not args.no_read_peak:
+        rp = read_peak(torch, stream)
+        result["read_peak"] = rp
         for key in ("roofline", "roofline_verify"):
-            result[key]["frac_of_copy_peak"] = round(result[key]["achieved"] / peak, 4)
+            result[key]["frac_of_read_peak"] = round(result[key]["achieved"] / rp["GBps"], 4)
+        for cfg in result.get("configs", {}).values():
+            for part in cfg.get("kernels", {}).values():
+                part["frac_of_read_peak"] = round(part["achieved_GBps"] / rp["GBps"], 4)
 
     # ---- CPU baseline: the oracle, as it stands, on a bounded sample --------------
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, head, hv, hd, args.cpu_cycles, with_commit, state_bytes)
     print(json.dumps(result), flush=True)
+
+
+def _stage_events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def _kernel_entry(name, launch_bytes, avg_s, flops=None):
+    e = {"kernel": name, "avg_launch_us": round(avg_s * 1e6, 2), "algorithmic_bytes_per_launch": int(launch_bytes),
+         "achieved_GBps": round(launch_bytes / avg_s / 1e9, 1),
+         "frac": round(launch_bytes / avg_s / 1e9 / PEAK_HBM_GBPS, 4)}
+    if flops is not None:
+        e["mfma_frac_of_dense_bf16_peak"] = round(flops / avg_s / 1e12 / PEAK_BF16_TFLOPS, 4)
+    return e
+
+
+def _time_cycles(torch, stream, run, n, every):
+    """n cycles of run(c, events) back to back; events in every `every`-th cycle; returns
+    (seconds, {cycle: events})."""
+    for c in range(3):
+        run(c, None)
+    torch.cuda.synchronize()
+    evs = {c: _stage_events(torch, 5) for c in range(n) if c % every == 0}
+    t0 = time.perf_counter()
+    for c in range(n):
+        run(c, evs.get(c))
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, evs
+
+
+def _span_avg(evs, a, b, div=1):
+    return float(np.mean([e[a].elapsed_time(e[b]) for e in evs.values()])) * 1e-3 / div
+
+
+def bench_batched(torch, mtp, synth, dh, nd, stream, n, every, state_bytes, kv_row_bytes):
+    """16 requests x 8 verify rows on the model-scale bf16 head: 7 draft-head calls of 16 rows,
+    the 128-row verify (wide kernel + per-row merge), acceptance, and the commit of 16 x 36 MiB
+    snapshots with the KV trim.  Raw random hidden rows, greedy."""
+    wl = synth.WORKLOADS["batched_commit"]
+    B, k, V, d = wl.B, wl.k, wl.V, wl.d
+    rng = np.random.default_rng(wl.seed + 1)
+    h_v, h_d = synth.make_hidden(rng, B, k, d)
+    hv = torch.from_numpy(synth.encode_hidden(h_v, "bf16").view(np.int16)).cuda()
+    hds = [torch.from_numpy(np.ascontiguousarray(synth.encode_hidden(h_d, "bf16")[:, i]).view(np.int16)).cuda()
+           for i in range(k)]
+    dtok = torch.zeros(B, k, dtype=torch.int32, device="cuda")
+    dst, vst = mtp.row_stats_empty(B, k), mtp.row_stats_empty(B, k + 1)
+    out = torch.zeros(B, k + 1, dtype=torch.int32, device="cuda")
+    nacc, nemit, flg = (torch.zeros(B, dtype=torch.int32, device="cuda") for _ in range(3))
+    ws = mtp.workspace(max(mtp.workspace_bytes(mtp.OP_DRAFT, B, nd, B), mtp.workspace_bytes(mtp.OP_VERIFY, B * (k + 1), V, B),
+                           mtp.workspace_bytes(mtp.OP_ACCEPT, 0, V, B)))
+    g = torch.Generator(device="cuda").manual_seed(5)
+    snaps = torch.randint(0, 256, (B, k + 1, state_bytes), dtype=torch.uint8, device="cuda", generator=g)
+    live = torch.zeros(B, state_bytes, dtype=torch.uint8, device="cuda")
+    kv_rows = KV_ROWS + (k + 1) * (n + 8)
+    kv = torch.zeros(B, KV_LAYERS, 2, kv_rows, kv_row_bytes, dtype=torch.uint8, device="cuda")
+    kv_len = torch.zeros(B, dtype=torch.int32, device="cuda")
+
+    def run(c, e):
+        smp = mtp.sampling(0.0, -1, 0, c, 0)
+        if e:
+            e[0].record(stream)
+        for i in range(k):
+            mtp.mtp_draft_head(dh, nd, hds[i], i, k, smp, dtok, dst, None, ws, stream)
+        if e:
+            e[1].record(stream)
+        mtp.mtp_verify_logits(dh, hv, k, dtok, k, smp, vst, None, ws, stream)
+        if e:
+            e[2].record(stream)
+        mtp.mtp_accept_sample(B, k, k, V, nd, smp, dtok, dst, None, vst, None, out, nacc, nemit, flg, ws, stream)
+        if e:
+            e[3].record(stream)
+        mtp.mtp_commit_state(B, k, nacc, snaps, live, state_bytes, kv, KV_LAYERS, kv_rows, kv_row_bytes, kv_len,
+                             stream)
+        if e:
+            e[4].record(stream)
+
+    el, evs = _time_cycles(torch, stream, run, n, every)
+    d_s, v_s, a_s, c_s = _span_avg(evs, 0, 1, k), _span_avg(evs, 1, 2), _span_avg(evs, 2, 3), _span_avg(evs, 3, 4)
+    draft_bytes = nd * 2 * d + B * 2 * d + B * 36
+    verify_bytes = V * 2 * d + B * (k + 1) * (2 * d + 32)
+    commit_bytes = 2 * B * state_bytes
+    r = {"workload": "batched_16x8", "requests": B, "verify_rows": B * (k + 1), "cycles": n,
+         "step": f"{k} draft-head calls ({B} rows) + verify ({B * (k + 1)} rows) + accept + commit "
+                 f"({B} x 36 MiB snapshot select, 12-layer KV trim)",
+         "cycles_per_s": round(n / el, 2),
+         "kernel_timing": "HIP events on the launch stream in every " + str(every) + "th cycle (the verify span "
+                          "covers the wide kernel and its per-row merge)",
+         "kernels": {"draft_head_16_rows": _kernel_entry("mtp_draft_head_kernel", draft_bytes, d_s),
+                     "verify_128_rows": _kernel_entry("mtp_verify_wide_kernel + mtp_verify_wide_merge_kernel",
+                                                      verify_bytes, v_s, flops=2.0 * V * d * B * (k + 1)),
+                     "commit": _kernel_entry("mtp_commit_state_kernel", commit_bytes, c_s)},
+         "accept_us": round(a_s * 1e6, 2)}
+    del snaps, live, kv
+    return r
+
+
+def bench_q4(torch, mtp, synth, stream, n, every, state_bytes, kv_row_bytes):
+    """The 4-bit affine head (152,064 x 2560, 32-value groups, bf16 scale and min, tiled):
+    7 draft-head calls, the 8-row verify, acceptance and the commit of one request, greedy,
+    raw random hidden rows (the q4_greedy workload's draws)."""
+    wl = synth.WORKLOADS["q4_greedy"]
+    B, k, V, d, nd = wl.B, wl.k, wl.V, wl.d, wl.n_draft
+    rng = np.random.default_rng(wl.seed)
+    head = synth.make_head(rng, V, d, "q4a32")
+    h_v, h_d = synth.make_hidden(rng, B, k, d)
+    dh = mtp.tiled_head(mtp.Head(mtp.W_Q4A32, d, V, torch.from_numpy(head.w).cuda(),
+                                 torch.from_numpy(head.scale.view(np.int16)).cuda(),
+                                 torch.from_numpy(head.minv.view(np.int16)).cuda()))
+    torch.cuda.synchronize()
+    hv = torch.from_numpy(synth.encode_hidden(h_v, "bf16").view(np.int16)).cuda()
+    hds = [torch.from_numpy(np.ascontiguousarray(synth.encode_hidden(h_d, "bf16")[:, i]).view(np.int16)).cuda()
+           for i in range(k)]
+    dtok = torch.zeros(B, k, dtype=torch.int32, device="cuda")
+    dst, vst = mtp.row_stats_empty(B, k), mtp.row_stats_empty(B, k + 1)
+    out = torch.zeros(B, k + 1, dtype=torch.int32, device="cuda")
+    nacc, nemit, flg = (torch.zeros(B, dtype=torch.int32, device="cuda") for _ in range(3))
+    ws = mtp.workspace(max(mtp.workspace_bytes(mtp.OP_DRAFT, B, nd, B), mtp.workspace_bytes(mtp.OP_VERIFY, B * (k + 1), V, B),
+                           mtp.workspace_bytes(mtp.OP_ACCEPT, 0, V, B)))
+    g = torch.Generator(device="cuda").manual_seed(6)
+    snaps = torch.randint(0, 256, (B, k + 1, state_bytes), dtype=torch.uint8, device="cuda", generator=g)
+    live = torch.zeros(B, state_bytes, dtype=torch.uint8, device="cuda")
+    kv_rows = KV_ROWS + (k + 1) * (n + 8)
+    kv = torch.zeros(B, KV_LAYERS, 2, kv_rows, kv_row_bytes, dtype=torch.uint8, device="cuda")
+    kv_len = torch.zeros(B, dtype=torch.int32, device="cuda")
+
+    def run(c, e):
+        smp = mtp.sampling(0.0, -1, 0, c, 0)
+        if e:
+            e[0].record(stream)
+        for i in range(k):
+            mtp.mtp_draft_head(dh, nd, hds[i], i, k, smp, dtok, dst, None, ws, stream)
+        if e:
+            e[1].record(stream)
+        mtp.mtp_verify_logits(dh, hv, k, dtok, k, smp, vst, None, ws, stream)
+        if e:
+            e[2].record(stream)
+        mtp.mtp_accept_sample(B, k, k, V, nd, smp, dtok, dst, None, vst, None, out, nacc, nemit, flg, ws, stream)
+        if e:
+            e[3].record(stream)
+        mtp.mtp_commit_state(B, k, nacc, snaps, live, state_bytes, kv, KV_LAYERS, kv_rows, kv_row_bytes, kv_len,
+                             stream)
+        if e:
+            e[4].record(stream)
+
+    el, evs = _time_cycles(torch, stream, run, n, every)
+    d_s, v_s, a_s, c_s = _span_avg(evs, 0, 1, k), _span_avg(evs, 1, 2), _span_avg(evs, 2, 3), _span_avg(evs, 3, 4)
+    wrow = d // 2 + 2 * 2 * (d // 32)
+    draft_bytes = nd * wrow + B * 2 * d + B * 36
+    verify_bytes = V * wrow + B * (k + 1) * (2 * d + 32)
+    r = {"workload": "q4_greedy", "cycles": n, "weights": "4-bit affine, 32-value groups, bf16 scale and min (1,600 B/row)",
+         "step": f"{k} draft-head calls + verify ({B * (k + 1)} rows) + accept + commit (36 MiB snapshot select)",
+         "cycles_per_s": round(n / el, 2),
+         "kernel_timing": "HIP events on the launch stream in every " + str(every) + "th cycle",
+         "kernels": {"draft_head": _kernel_entry("mtp_draft_head_kernel", draft_bytes, d_s),
+                     "verify_8_rows": _kernel_entry("mtp_verify_logits_kernel", verify_bytes, v_s)},
+         "accept_us": round(a_s * 1e6, 2), "commit_us": round(c_s * 1e6, 2)}
+    del snaps, live, kv, dh
+    return r
+
+
+def read_peak(torch, stream, nbytes: int = 1 << 30):
+    """Read-only bandwidth ceiling: libmtp_probe's stream_read over nbytes (4x the 256 MB
+    last-level cache), every depth x grid shape, best of 5 launches each; bytes read / time."""
+    import ctypes
+    from speculative_decoding_head_amd import build as _b
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.mtp_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mtp_probe_stream_read.restype = ctypes.c_int
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)                       # every lane's fold is 0 or 0x01010101, never the magic value
+    grids, depths = (256, 512, 1024, 2048), (8, 16, 32)
+    sink = torch.zeros(max(grids) * 512, dtype=torch.int32, device="cuda")
+    sp = stream.cuda_stream
+    table = {}
+    for depth in depths:
+        for grid in grids:
+            def launch():
+                rc = lib.mtp_probe_stream_read(buf.data_ptr(), nbytes, grid, depth, 0x9E3779B9, sink.data_ptr(), sp)
+                if rc != 0:
+                    raise RuntimeError(f"stream probe failed ({rc})")
+            launch()
+            torch.cuda.synchronize()
+            best = None
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                launch()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t = e0.elapsed_time(e1) * 1e-3
+                best = t if best is None else min(best, t)
+            table[f"depth{depth}_grid{grid}"] = round(nbytes / best / 1e9, 1)
+    del buf, sink
+    torch.cuda.empty_cache()
+    key = max(table, key=table.get)
+    return {"GBps": table[key], "shape": key, "frac_of_8TBps": round(table[key] / PEAK_HBM_GBPS, 4),
+            "kind": "read-only stream of 1 GiB (libmtp_probe: 1 KiB per wave non-temporal loads, the tiled "
+                    "LM-head pattern, no arithmetic), best of 5 launches per shape, best shape",
+            "shapes_GBps": table}
 
 
 def cpu_model() -> str:
