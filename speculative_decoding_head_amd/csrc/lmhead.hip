@@ -224,25 +224,54 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
     }
     return v;
   };
-  constexpr int kPreFrags = 80 / kWaves;   // d = 2560 at 16 rows: 5,120 fragments per block
-  uint4 hv[kPreFrags];
-#pragma unroll
-  for (int q = 0; q < kPreFrags; ++q)
-    if (tid + q * kThreads < nfrag) hv[q] = hfrag(tid + q * kThreads);
   Chunk A, B;
   uint32_t roff_cur[TV], roff_nxt[TV];
-  row_offsets(t_begin, roff_cur);
-  load(A, roff_cur, 0);
+  if constexpr (!L::q4) {
+    constexpr int kPreFrags = 80 / kWaves;   // d = 2560 at 16 rows: 5,120 fragments per block
+    uint4 hv[kPreFrags];
 #pragma unroll
-  for (int q = 0; q < kPreFrags; ++q)
-    if (tid + q * kThreads < nfrag) frag[tid + q * kThreads] = hv[q];
-  for (int f = tid + kPreFrags * kThreads; f < nfrag; f += kThreads) frag[f] = hfrag(f);
-  if (L::q4) {
-    // per 32-value group and hidden row: sum of the hidden values
-    for (int e = tid; e < nsteps * 16; e += kThreads) {
-      const int s = e >> 4, i = e & 15;
-      htab[e] = i < M ? group_sum32(static_cast<const uint16_t*>(p.hidden) + (size_t)i * d + 32 * s) : 0.0f;
+    for (int q = 0; q < kPreFrags; ++q)
+      if (tid + q * kThreads < nfrag) hv[q] = hfrag(tid + q * kThreads);
+    row_offsets(t_begin, roff_cur);
+    load(A, roff_cur, 0);
+#pragma unroll
+    for (int q = 0; q < kPreFrags; ++q)
+      if (tid + q * kThreads < nfrag) frag[tid + q * kThreads] = hv[q];
+    for (int f = tid + kPreFrags * kThreads; f < nfrag; f += kThreads) frag[f] = hfrag(f);
+  } else {
+    // 4-bit heads: a thread stages the four quarters of one (step, row) unit and their group
+    // sum (the factor of the group's min), so the sums cost no extra round trip to memory
+    const int nunit = nsteps * M;
+    const uint16_t* hid = static_cast<const uint16_t*>(p.hidden);
+    auto unit_load = [&](int unit, uint4 (&v)[4]) {
+      const int s = unit / M, i = unit % M;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) v[gg] = *reinterpret_cast<const uint4*>(hid + (size_t)i * d + 32 * s + 8 * gg);
+    };
+    auto unit_store = [&](int unit, const uint4 (&v)[4]) {
+      const int s = unit / M, i = unit % M;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) frag[(s * 4 + gg) * M + i] = q4_order(v[gg]);
+      htab[s * 16 + i] = group_sum_quarters(v);
+    };
+    constexpr int kPreUnits = 3;   // d = 2560 at 16 rows: 1,280 units per block
+    uint4 hv[kPreUnits][4];
+#pragma unroll
+    for (int q = 0; q < kPreUnits; ++q)
+      if (tid + q * kThreads < nunit) unit_load(tid + q * kThreads, hv[q]);
+    row_offsets(t_begin, roff_cur);
+    load(A, roff_cur, 0);
+#pragma unroll
+    for (int q = 0; q < kPreUnits; ++q)
+      if (tid + q * kThreads < nunit) unit_store(tid + q * kThreads, hv[q]);
+    for (int unit = tid + kPreUnits * kThreads; unit < nunit; unit += kThreads) {
+      uint4 v[4];
+      unit_load(unit, v);
+      unit_store(unit, v);
     }
+    // rows no launch row occupies
+    for (int e = tid; e < nsteps * 16; e += kThreads)
+      if ((e & 15) >= M) htab[e] = 0.0f;
   }
   __syncthreads();
 

@@ -57,25 +57,29 @@ __device__ __forceinline__ uint4 q4_order(uint4 v) {
                (v.z & 0xFFFFu) | (v.w << 16), (v.z >> 16) | (v.w & 0xFFFF0000u)};
 }
 
-// Sum of one 32-value group of bf16 hidden values (64 contiguous, 16-byte aligned bytes) in
-// one fixed order that every kernel uses: each quarter of 8 values left to right, then
-// (q0 + q1) + (q2 + q3).
-__device__ __forceinline__ float group_sum32(const uint16_t* h) {
-  float q[4];
+// Sum of one 32-value group of bf16 hidden values in one fixed order that every kernel
+// uses: each quarter of 8 values left to right, then (q0 + q1) + (q2 + q3).
+__device__ __forceinline__ float quarter_sum8(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float a = __uint_as_float(w[0] << 16);
+  a += __uint_as_float(w[0] & 0xFFFF0000u);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const uint4 v = *reinterpret_cast<const uint4*>(h + 8 * c);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float a = __uint_as_float(w[0] << 16);
-    a += __uint_as_float(w[0] & 0xFFFF0000u);
-#pragma unroll
-    for (int e = 1; e < 4; ++e) {
-      a += __uint_as_float(w[e] << 16);
-      a += __uint_as_float(w[e] & 0xFFFF0000u);
-    }
-    q[c] = a;
+  for (int e = 1; e < 4; ++e) {
+    a += __uint_as_float(w[e] << 16);
+    a += __uint_as_float(w[e] & 0xFFFF0000u);
   }
-  return (q[0] + q[1]) + (q[2] + q[3]);
+  return a;
+}
+// the group from its four quarters (raw memory order, 8 values each)
+__device__ __forceinline__ float group_sum_quarters(const uint4 (&v)[4]) {
+  return (quarter_sum8(v[0]) + quarter_sum8(v[1])) + (quarter_sum8(v[2]) + quarter_sum8(v[3]));
+}
+// the group from memory (64 contiguous, 16-byte aligned bytes)
+__device__ __forceinline__ float group_sum32(const uint16_t* h) {
+  uint4 v[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v[c] = *reinterpret_cast<const uint4*>(h + 8 * c);
+  return group_sum_quarters(v);
 }
 
 template <int WT>
