@@ -70,6 +70,10 @@ def parse():
                          "gathered once into their own head; 0 = the first n_draft ids")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-commit", action="store_true", help="leave the commit out of the step")
+    ap.add_argument("--overlap-commit", action="store_true",
+                    help="run each cycle's commit on a second stream beside the next cycle's draft calls (the next "
+                         "verify waits for it) instead of on the launch stream after the accept; measured slower: "
+                         "the copy and the draft head share HBM")
     ap.add_argument("--no-read-peak", action="store_true", help="skip the 1 GiB read-ceiling measurement")
     ap.add_argument("--no-extra-configs", action="store_true",
                     help="model_greedy only: skip timing the 16 x 8-row batched cycle and the 4-bit head cycle")
@@ -292,6 +296,13 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    # --overlap-commit: the commit of a cycle runs on a second stream, beside the next cycle's
+    # draft calls (they do not read the recurrent state or kv_len; the next verify does, and
+    # waits for it)
+    commit_stream = torch.cuda.Stream() if (with_commit and args.overlap_commit) else None
+    ev_acc, ev_commit = torch.cuda.Event(), torch.cuda.Event()
+    commit_pending = [False]
+
     def cycle(c, events=None, hidden=None):
         hv_c, hd_c = (hv_t, hd_slots) if hidden is None else hidden
         smp = mtp.sampling(T, wl.eos, wl.philox_seed, c, 0, rule, positions if exact else None)
@@ -303,6 +314,9 @@ def main():
             mtp.mtp_draft_head(ddh, nd, hd_c[i], i, k, smp, dtok, dst, dlg, ws, stream)
         if events is not None:
             events[1].record(stream)
+        if commit_pending[0]:
+            stream.wait_event(ev_commit)   # the verify reads the committed state and kv_len
+            commit_pending[0] = False
         mtp.mtp_verify_logits(dh, hv_c, k, dtok, k, smp, vst, vlg, ws, stream)
         if events is not None:
             events[2].record(stream)
@@ -310,11 +324,20 @@ def main():
                               draft_row_of=row_of)
         if events is not None:
             events[3].record(stream)
-        if with_commit:
+        if with_commit and commit_stream is None:
             mtp.mtp_commit_state(B, k, nacc, snaps, live, state_bytes, kv, KV_LAYERS, kv_rows, kv_row_bytes,
                                  kv_len, stream)
             if events is not None:
                 events[4].record(stream)
+        elif with_commit:
+            ev_acc.record(stream)
+            commit_stream.wait_event(ev_acc)
+            mtp.mtp_commit_state(B, k, nacc, snaps, live, state_bytes, kv, KV_LAYERS, kv_rows, kv_row_bytes,
+                                 kv_len, commit_stream)
+            ev_commit.record(commit_stream)
+            commit_pending[0] = True
+            if events is not None:
+                events[4].record(commit_stream)
 
     if args.calibrate_copy:
         # a plain kernel copy of known size (multiply by one: reads and writes COPY_BYTES);
@@ -412,12 +435,16 @@ def main():
                                         f"{min(args.draft_ids, nd):,} ids" if draft_ids is not None else
                                         f"the first {nd:,} ids"),
                    "step": f"{k} draft-head calls + verify ({B * (k + 1)} rows) + accept"
-                           + (" + commit (36 MiB snapshot select, 12-layer KV trim)" if with_commit else "")},
+                           + (" + commit (36 MiB snapshot select, 12-layer KV trim)" if with_commit else ""),
+                   "commit_stream": ("second stream, beside the next cycle's draft calls (the next verify waits "
+                                     "for it)" if commit_stream is not None else "the launch stream")
+                                    if with_commit else None},
         "roofline": roofline,
         "roofline_verify": roof(verify_bytes, v_avg, verify_kernel, flops=2.0 * V * d * B * (k + 1)),
         "kernel_timing": f"HIP events on the launch stream in {len(timed)} of the {args.steps} timed cycles: "
                          f"one pair around the {k} back-to-back draft launches (average = span / {k}), "
-                         f"one pair around each of verify, accept and commit",
+                         f"one pair around each of verify, accept and commit (the commit's from the end of "
+                         f"the accept to the end of the commit on its own stream)",
         "stages_us": {"draft_head_avg": round(d_avg * 1e6, 2), "verify_avg": round(v_avg * 1e6, 2),
                       "accept_avg": round(float(np.mean(accept_ms)) * 1e3, 2),
                       "commit_avg": round(float(np.mean(commit_ms)) * 1e3, 2)},
