@@ -294,8 +294,9 @@ int mtp_commit_state(int32_t B, int32_t k, const int32_t* n_accept, const void* 
  * loops or harnesses that forbid hipMalloc): mtp_verify_logits without a workspace.  The
  * scratch the verify kernels need lives in a device array inside the library, 1,573,632
  * bytes per GPU (enough for any valid call: up to 128 rows, any vocabulary), held until
- * the process ends; its address is resolved, and its completion ticket cleared, on the
- * first call on each device.  The call allocates nothing.  Results are those of
+ * the process ends; the array used is that of the device the stream runs on (the current
+ * device for the null stream), and its address is resolved, and its completion ticket
+ * cleared, on the first call on each device.  The call allocates nothing.  Results are those of
  * mtp_verify_logits, bit for bit.  All calls on one GPU share the array and each leaves
  * it ready for the next: calls that overlap on one GPU (other streams, other host
  * threads) race and must be ordered by the caller.  MTP_ERR_WORKSPACE if a call would

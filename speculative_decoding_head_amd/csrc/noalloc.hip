@@ -34,17 +34,28 @@ std::once_flag g_once[kMaxDevices];
 void* g_ptr[kMaxDevices];
 hipError_t g_err[kMaxDevices];
 
-// The device address of this device's scratch array (nullptr on failure); cleared on first use.
+// The device address of the scratch array of the device the stream runs on (the current
+// device for the null stream), or nullptr on failure.  The first call on a device resolves
+// the address with that device current (restoring the caller's current device after) and
+// clears the ticket on the stream.
 void* device_scratch(hipStream_t stream) {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  const hipError_t q = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (q != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
   std::call_once(g_once[dev], [dev, stream]() {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
     void* ptr = nullptr;
-    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
     if (e == hipSuccess && ptr != nullptr) {
       // the completion ticket and the drafted-id slots (the first 768 bytes) start at zero
       hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, stream, static_cast<uint32_t*>(ptr), 192);
       e = hipGetLastError();
+    }
+    if (cur >= 0 && cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
     }
     g_err[dev] = e;
     g_ptr[dev] = e == hipSuccess ? ptr : nullptr;

@@ -30,14 +30,15 @@ def _inputs(rng, head, B, k, d, V):
     return hv, drafts
 
 
-def _both(dh, hv, drafts, B, k, T, V):
+def _both(dh, hv, drafts, B, k, T, V, stream=None):
     smp = mtp.sampling(T, -1, 4321, 7, 0)
     out = []
     for noalloc in (False, True):
         st = mtp.row_stats_empty(B, k + 1)
         lg = torch.full((B, k + 1, V), 7.0, dtype=torch.float32, device="cuda") if T > 0 else None
+        torch.cuda.synchronize()
         if noalloc:
-            mtp.mtp_verify_logits_noalloc(dh, hv, k, drafts, 7, smp, st, lg)
+            mtp.mtp_verify_logits_noalloc(dh, hv, k, drafts, 7, smp, st, lg, stream)
         else:
             ws = mtp.workspace(mtp.workspace_bytes(mtp.OP_VERIFY, B * (k + 1), V, B))
             mtp.mtp_verify_logits(dh, hv, k, drafts, 7, smp, st, lg, ws)
@@ -72,6 +73,24 @@ def test_noalloc_verify_at_model_scale():
     hv, drafts = _inputs(rng, head, 1, wl.k, wl.d, wl.V)
     (st_ws, _), (st_na, _) = _both(dh, hv, drafts, 1, wl.k, 0.0, wl.V)
     assert np.array_equal(st_ws, st_na)
+
+
+@pytest.mark.gpu
+def test_noalloc_verify_on_a_side_stream():
+    """The scratch array is found through the stream's own device (not only the null stream),
+    and calls on another stream of the same device, ordered by synchronisation, give the
+    same bits."""
+    V, d = 4099, 256
+    rng = np.random.default_rng(29)
+    head = synth.make_head(rng, V, d, "bf16")
+    dh = dev_head(head, tiled=True)
+    side = torch.cuda.Stream()
+    for B, k, T in ((16, 7, 1.0), (2, 5, 0.0)):
+        hv, drafts = _inputs(rng, head, B, k, d, V)
+        (st_ws, lg_ws), (st_na, lg_na) = _both(dh, hv, drafts, B, k, T, V, stream=side)
+        assert np.array_equal(st_ws, st_na), (B, k, T)
+        if T > 0:
+            assert np.array_equal(lg_ws.view(np.uint32), lg_na.view(np.uint32)), (B, k, T)
 
 
 def test_noalloc_rejects_bad_arguments_before_touching_a_device():
