@@ -624,12 +624,17 @@ def _stage_events(torch, n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
-def _kernel_entry(name, launch_bytes, avg_s, flops=None):
+def _kernel_entry(name, launch_bytes, avg_s, flops=None, traffic_of=None):
+    """traffic_of: (workload, [kernel keys]) whose counter-measured HBM bytes per launch
+    (profiles/traffic.json, while it matches these sources) are summed into "traffic"."""
     e = {"kernel": name, "avg_launch_us": round(avg_s * 1e6, 2), "algorithmic_bytes_per_launch": int(launch_bytes),
          "achieved_GBps": round(launch_bytes / avg_s / 1e9, 1),
          "frac": round(launch_bytes / avg_s / 1e9 / PEAK_HBM_GBPS, 4)}
     if flops is not None:
         e["mfma_frac_of_dense_bf16_peak"] = round(flops / avg_s / 1e12 / PEAK_BF16_TFLOPS, 4)
+    if traffic_of is not None:
+        parts = [load_traffic(traffic_of[0], k) for k in traffic_of[1]]
+        e["traffic"] = None if any(t is None for t in parts) else int(sum(parts))
     return e
 
 
@@ -705,10 +710,14 @@ def bench_batched(torch, mtp, synth, dh, nd, stream, n, every, state_bytes, kv_r
          "cycles_per_s": round(n / el, 2),
          "kernel_timing": "HIP events on the launch stream in every " + str(every) + "th cycle (the verify span "
                           "covers the wide kernel and its per-row merge)",
-         "kernels": {"draft_head_16_rows": _kernel_entry("mtp_draft_head_kernel", draft_bytes, d_s),
+         "kernels": {"draft_head_16_rows": _kernel_entry("mtp_draft_head_kernel", draft_bytes, d_s,
+                                                         traffic_of=("batched_commit", ["mtp_draft_head_kernel"])),
                      "verify_128_rows": _kernel_entry("mtp_verify_wide_kernel + mtp_verify_wide_merge_kernel",
-                                                      verify_bytes, v_s, flops=2.0 * V * d * B * (k + 1)),
-                     "commit": _kernel_entry("mtp_commit_state_kernel", commit_bytes, c_s)},
+                                                      verify_bytes, v_s, flops=2.0 * V * d * B * (k + 1),
+                                                      traffic_of=("batched_commit", ["mtp_verify_wide_kernel",
+                                                                                      "mtp_verify_wide_merge_kernel"])),
+                     "commit": _kernel_entry("mtp_commit_state_kernel", commit_bytes, c_s,
+                                             traffic_of=("batched_commit", ["mtp_commit_state_kernel"]))},
          "accept_us": round(a_s * 1e6, 2)}
     del snaps, live, kv
     return r
@@ -771,8 +780,10 @@ def bench_q4(torch, mtp, synth, stream, n, every, state_bytes, kv_row_bytes):
          "step": f"{k} draft-head calls + verify ({B * (k + 1)} rows) + accept + commit (36 MiB snapshot select)",
          "cycles_per_s": round(n / el, 2),
          "kernel_timing": "HIP events on the launch stream in every " + str(every) + "th cycle",
-         "kernels": {"draft_head": _kernel_entry("mtp_draft_head_kernel", draft_bytes, d_s),
-                     "verify_8_rows": _kernel_entry("mtp_verify_logits_kernel", verify_bytes, v_s)},
+         "kernels": {"draft_head": _kernel_entry("mtp_draft_head_kernel", draft_bytes, d_s,
+                                                 traffic_of=("q4_greedy", ["mtp_draft_head_kernel"])),
+                     "verify_8_rows": _kernel_entry("mtp_verify_logits_kernel", verify_bytes, v_s,
+                                                    traffic_of=("q4_greedy", ["mtp_verify_logits_kernel"]))},
          "accept_us": round(a_s * 1e6, 2), "commit_us": round(c_s * 1e6, 2)}
     del snaps, live, kv, dh
     return r
