@@ -66,14 +66,17 @@ def test_noalloc_verify_equals_the_workspace_verify(tiled):
 
 @pytest.mark.gpu
 def test_noalloc_verify_at_model_scale():
-    """The model-scale verify (152,064 x 2560 bf16, tiled, 8 rows) on the scratch array."""
+    """The model-scale verify (152,064 x 2560 bf16, tiled) on the scratch array: one request's
+    8 rows, then 16 requests x 8 rows (the 128-row kernel over 198 blocks, the most scratch a
+    call of this head uses), then 8 rows again."""
     wl = synth.WORKLOADS["model_greedy"]
     rng = np.random.default_rng(wl.seed)
     head = synth.make_head(rng, wl.V, wl.d, wl.wtype)
     dh = dev_head(head, tiled=True)
-    hv, drafts = _inputs(rng, head, 1, wl.k, wl.d, wl.V)
-    (st_ws, _), (st_na, _) = _both(dh, hv, drafts, 1, wl.k, 0.0, wl.V)
-    assert np.array_equal(st_ws, st_na)
+    for B in (1, 16, 1):
+        hv, drafts = _inputs(rng, head, B, wl.k, wl.d, wl.V)
+        (st_ws, _), (st_na, _) = _both(dh, hv, drafts, B, wl.k, 0.0, wl.V)
+        assert np.array_equal(st_ws, st_na), B
 
 
 @pytest.mark.gpu
