@@ -41,14 +41,15 @@ constexpr int kTV = 1;               // 16-row vocabulary tiles per wave per pas
 constexpr int kU = 8;                // K steps per prefetch chunk
 constexpr int kTVQ4 = 2;             // the same for 4-bit heads, whose K steps carry a
 constexpr int kUQ4 = 8;              // quarter of the bytes
-// 4-bit heads under sampling keep the Gumbel state live through the K loop: one tile per
-// pass keeps them out of scratch (two spilled 108-156 bytes per lane and ran 9-11% slower)
+// 4-bit heads under sampling keep the Gumbel state of four hidden rows live through the K
+// loop: one tile per pass keeps them out of scratch (two spilled 128-180 bytes per lane and
+// ran 9-11% slower); the one-row draft head holds two without spilling
 constexpr int kTVQ4S = 1;
 
-// tiles per wave pass of a launch
-template <int WT, bool SAMPLED>
+// tiles per wave pass of a launch (RL: accumulator rows a lane holds live)
+template <int WT, bool SAMPLED, int RL = 4>
 constexpr int tiles_per_pass() {
-  return Layout<WT>::q4 ? (SAMPLED ? kTVQ4S : kTVQ4) : kTV;
+  return Layout<WT>::q4 ? ((SAMPLED && RL != 1) ? kTVQ4S : kTVQ4) : kTV;
 }
 constexpr int kMaxGrid = 256;        // blocks per launch (partials per row in the workspace)
 
@@ -70,7 +71,7 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   const int xi = lane & 15, g = lane >> 4;
   const int M = p.M, d = p.d;
   using L = Layout<WT>;
-  constexpr int TV = tiles_per_pass<WT, SAMPLED>();
+  constexpr int TV = tiles_per_pass<WT, SAMPLED, RL>();
   constexpr int U = L::q4 ? kUQ4 : kU;
   static_assert(!L::q4 || U % 8 == 0, "4-bit chunks cover whole octets of groups (one scale vector each)");
   const int nsteps = L::f32 ? d / 16 : d / 32;
@@ -529,12 +530,13 @@ static int lmhead_launch_grid(int n_rows, int tv) {
 
 template <int WT, bool SAMPLED>
 static hipError_t launch_t(const LmheadLaunch& p, hipStream_t stream) {
-  const int G = lmhead_launch_grid(p.n_rows, tiles_per_pass<WT, SAMPLED>());
-  const size_t lds = lmhead_lds_bytes(WT, p.d, p.M);
   // the one-row specialisation only changes 4-bit heads' code
+  const bool one_row = Layout<WT>::q4 && !p.verify && p.M == 1;
+  const int G = lmhead_launch_grid(p.n_rows, one_row ? tiles_per_pass<WT, SAMPLED, 1>() : tiles_per_pass<WT, SAMPLED, 4>());
+  const size_t lds = lmhead_lds_bytes(WT, p.d, p.M);
   auto kern = p.verify ? mtp_verify_logits_kernel<WT, SAMPLED> : mtp_draft_head_kernel<WT, SAMPLED, 4>;
   if constexpr (Layout<WT>::q4)
-    if (!p.verify && p.M == 1) kern = mtp_draft_head_kernel<WT, SAMPLED, 1>;
+    if (one_row) kern = mtp_draft_head_kernel<WT, SAMPLED, 1>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
