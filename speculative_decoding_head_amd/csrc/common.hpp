@@ -81,22 +81,27 @@ __device__ __forceinline__ float sanitize(float z, uint32_t row_flags) {
 // ---------------------------------------------------------------------------------
 // Running statistics of one hidden row over a set of vocabulary rows.  Within one
 // lane ids are pushed in increasing order, so a strict '>' keeps the lowest id on ties;
-// merges compare ids explicitly.  48 bytes.
+// merges compare ids explicitly.  48 bytes; the first 32 hold every field a row scored
+// without sampling changes (the rest keep their initial values there).
 // ---------------------------------------------------------------------------------
 struct RowAcc {
   float m;        // max of finite z / T_eff (-inf if none yet)
   float s;        // sum of exp(z / T_eff - m) over finite z
   float zmax;     // max finite z
   int imax;       // its lowest id (kNoIndex if none)
-  float gbest;    // best z / T + Gumbel over finite z
-  int gidx;       // its id
-  float gz;       // z at gidx
   int nonfinite;  // count of NaN / +-inf
   int nposinf;    // count of +inf
   int pinf_min;   // lowest +inf id
+  int pgidx;      // id of the best Gumbel among +inf ids
+  float gbest;    // best z / T + Gumbel over finite z
+  int gidx;       // its id
+  float gz;       // z at gidx
   float pg;       // best Gumbel among +inf ids (their sanitised logit is 0)
-  int pgidx;
 };
+// 16-byte pieces of a RowAcc that a merge needs: all three under sampling, the first two
+// otherwise
+template <bool SAMPLED>
+constexpr int rowacc_pieces() { return SAMPLED ? 3 : 2; }
 
 __device__ __forceinline__ void rowacc_init(RowAcc& a) {
   a.m = kNegInf; a.s = 0.0f; a.zmax = kNegInf; a.imax = kNoIndex;

@@ -395,7 +395,7 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
   if (tid < M) {
     RowAcc a = red[tid];
     for (int w = 1; w < kWaves; ++w) rowacc_merge(a, red[w * 16 + tid]);
-    store_partial_fm(pr, tid, blockIdx.x, M, G, a);
+    store_partial_fm<rowacc_pieces<SAMPLED>()>(pr, tid, blockIdx.x, M, G, a);
   }
   wait_stores();
   __syncthreads();
@@ -427,7 +427,7 @@ __device__ __forceinline__ void lmhead_body(const LmheadLaunch& p) {
 #pragma unroll
       for (int q = 0; q < NP; ++q) {
         const int blk = lane + 64 * q;
-        if (jr[r] < M && blk < G) part[r][q] = load_partial_fm(pr, jr[r], blk, M, G);
+        if (jr[r] < M && blk < G) part[r][q] = load_partial_fm<rowacc_pieces<SAMPLED>()>(pr, jr[r], blk, M, G);
         else rowacc_init(part[r][q]);
       }
       zbits[r] = (VERIFY && jr[r] < M) ? load_coherent(reinterpret_cast<const uint32_t*>(ztok) + jr[r]) : 0u;

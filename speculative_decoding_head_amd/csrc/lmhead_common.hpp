@@ -87,23 +87,27 @@ __device__ __forceinline__ size_t row_bytes(int d) {
   return WT == MTP_W_F32 ? (size_t)d * 4 : (Layout<WT>::q4 ? (size_t)d / 2 : (size_t)d * 2);
 }
 
-// partials are handed between blocks as three 16-byte device-scope buffer stores/loads
+// partials are handed between blocks as 16-byte device-scope buffer stores/loads (NP of
+// the RowAcc's three pieces; a piece not loaded keeps its initial values)
 constexpr int kCoherent = 16;   // cache-policy bits: device scope (sc1)
 // field-major partials: 16-byte piece i of (row j, block b) at ((i * M + j) * G + b) * 16,
 // so that lanes reading consecutive blocks of one row read contiguous bytes
 __device__ __forceinline__ uint32_t partial_piece_off(int i, int j, int b, int M, int G) {
   return (uint32_t)((((size_t)i * M + j) * G + b) * 16);
 }
+template <int NP>
 __device__ __forceinline__ void store_partial_fm(__amdgpu_buffer_rsrc_t r, int j, int b, int M, int G, const RowAcc& a) {
   const u32x4* v = reinterpret_cast<const u32x4*>(&a);
 #pragma unroll
-  for (int i = 0; i < 3; ++i) __builtin_amdgcn_raw_buffer_store_b128(v[i], r, (int)partial_piece_off(i, j, b, M, G), 0, kCoherent);
+  for (int i = 0; i < NP; ++i) __builtin_amdgcn_raw_buffer_store_b128(v[i], r, (int)partial_piece_off(i, j, b, M, G), 0, kCoherent);
 }
+template <int NP>
 __device__ __forceinline__ RowAcc load_partial_fm(__amdgpu_buffer_rsrc_t r, int j, int b, int M, int G) {
   RowAcc a;
+  rowacc_init(a);
   u32x4* v = reinterpret_cast<u32x4*>(&a);
 #pragma unroll
-  for (int i = 0; i < 3; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)partial_piece_off(i, j, b, M, G), 0, kCoherent);
+  for (int i = 0; i < NP; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)partial_piece_off(i, j, b, M, G), 0, kCoherent);
   return a;
 }
 

@@ -730,7 +730,7 @@ __device__ __forceinline__ void wide_body(const LmheadLaunch& p) {
     u32x4* pf = reinterpret_cast<u32x4*>(static_cast<unsigned char*>(p.ws) + lmhead_partials_offset(M));
     const u32x4* av = reinterpret_cast<const u32x4*>(&a);
 #pragma unroll
-    for (int i = 0; i < 3; ++i) pf[((size_t)i * M + tid) * gridDim.x + blockIdx.x] = av[i];
+    for (int i = 0; i < rowacc_pieces<SAMPLED>(); ++i) pf[((size_t)i * M + tid) * gridDim.x + blockIdx.x] = av[i];
   }
 }
 
@@ -747,9 +747,10 @@ __device__ __forceinline__ void wide_merge_body(const LmheadLaunch& p, int G) {
   rowacc_init(a);
   for (int blk = tid; blk < G; blk += kMergeThreads) {
     RowAcc b;
+    rowacc_init(b);
     u32x4* bv = reinterpret_cast<u32x4*>(&b);
 #pragma unroll
-    for (int i = 0; i < 3; ++i) bv[i] = pf[((size_t)i * M + j) * G + blk];
+    for (int i = 0; i < rowacc_pieces<SAMPLED>(); ++i) bv[i] = pf[((size_t)i * M + j) * G + blk];
     rowacc_merge(a, b);
   }
 #pragma unroll
